@@ -1,0 +1,153 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so, the NVFP4 4-bit training hot path on AMD MI355X (gfx950).
+ *
+ * The library quantizes bf16/fp32 tensors to NVFP4, applies the random Hadamard transform to the
+ * weight-gradient operands, dequantizes, and multiplies two NVFP4 tensors with fp32
+ * accumulation.  An MXFP4 quantizer/GEMM is included as the comparison format.
+ *
+ * Citation keys for the web pages the operations follow:
+ *   [P1] "Entrenamiento de Modelos de Lenguaje con 4 Bits de Precision" (focoia.com.mx)
+ *   [P2] "FP4 All the Way: Formacion totalmente cuantificada de LLM" (slashpage.com summary)
+ *   [P3] "I ricercatori di Nvidia sbloccano il tutorial LLM a 8 bit che corrisponde alle
+ *        prestazioni a 4 bit" (massacarraranews.com)
+ *
+ * NVFP4 tensor format [P1 Caracteristicas del Formato NVFP4]:
+ *   - elements are E2M1 (1 sign, 2 exponent, 1 mantissa bit; values 0, .5, 1, 1.5, 2, 3, 4, 6
+ *     with either sign), packed two per byte: element 2j in the low nibble, 2j+1 in the high;
+ *   - every block of 16 contiguous elements along the reduction dimension K shares one E4M3
+ *     scale byte (OCP E4M3FN, non-negative, at most 448 = 0x7E); 16x16 tiles for weights
+ *     [P1 Metodologia: two-dimensional block scaling for weights];
+ *   - one fp32 per-tensor decode scale s_dec [P3 Come funziona NVFP4?: multi-level scaling]:
+ *     with A the tensor amax, s_dec = A / 2688; the block scale is E4M3(amax_b * 448 / A) and an
+ *     element code is E2M1(x * (2688 / A) / scale_b).  The value of a code is v * scale_b * s_dec.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers owned by the caller, 16-byte aligned; the library never
+ *     allocates or frees memory and keeps no state between calls, so calls on different streams
+ *     are independent.  `stream` is a hipStream_t (NULL = the default stream).
+ *   - Work is enqueued on `stream` and the call returns without synchronising the host.
+ *   - Argument and shape errors return a non-zero status before anything is enqueued.  A kernel
+ *     launch failure returns NVFP4_ERR_LAUNCH.  Kernels never trap.
+ *   - Inputs must be finite; for NaN/Inf inputs the outputs are unspecified.
+ *   - Row strides `ld` are in elements, ld >= cols, and ld * element size must be a multiple of
+ *     16 bytes.  Quantized buffers are dense (no stride).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,     /* a required pointer is NULL */
+    NVFP4_ERR_SHAPE = 2,    /* a dimension is negative, not a multiple of the block, or mismatched */
+    NVFP4_ERR_DTYPE = 3,    /* unknown dtype or rounding mode */
+    NVFP4_ERR_ALIGN = 4,    /* a pointer or row stride is not 16-byte aligned */
+    NVFP4_ERR_LAYOUT = 5,   /* a tensor's block layout is not allowed for this call */
+    NVFP4_ERR_LAUNCH = 6    /* the HIP runtime rejected a kernel launch */
+} nvfp4_status;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
+
+/* Forward-pass operands round to nearest (ties to the even code); gradients round
+ * stochastically [P2 Describir].  SR rounds |z| up to the next grid value with probability
+ * (|z| - lo) / (hi - lo), using a 16-bit uniform from Philox4x32-10 with key = seed and counter
+ * = (element index / 8) where the element index is row * cols + col of the OUTPUT tensor; the
+ * eight elements of one counter take the 16-bit halves of its four output words in order. */
+typedef enum { NVFP4_RNE = 0, NVFP4_SR = 1 } nvfp4_round;
+
+typedef enum {
+    NVFP4_BLK_1x16 = 0,     /* scales [rows x cols/16] */
+    NVFP4_BLK_16x16 = 1,    /* scales [rows/16 x cols/16] (weights) */
+    MXFP4_BLK_1x32 = 2      /* E8M0 scales [rows x cols/32], no per-tensor scale */
+} nvfp4_layout;
+
+/* One quantized matrix of logical shape [rows x cols]; cols is the contiguous reduction
+ * dimension K.  codes: rows * cols / 2 bytes.  amax / s_dec: one device fp32 each (NVFP4
+ * only; the quantizers write both). */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    float *amax;
+    float *s_dec;
+    int64_t rows;
+    int64_t cols;
+    int32_t layout;         /* nvfp4_layout */
+    int32_t reserved;       /* must be 0 */
+} nvfp4_tensor;
+
+/* Human-readable text for a status code (static storage). */
+const char *nvfp4_status_string(nvfp4_status s);
+
+/* Per-tensor amax: *amax_out = max |x| over x [rows x cols] (row stride ld).  This is the first
+ * level of the two-level scaling [P3 Come funziona NVFP4?].  amax_out is overwritten. */
+nvfp4_status nvfp4_amax(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                        float *amax_out, void *stream);
+
+/* amax of the random-Hadamard-transformed tensor (see nvfp4_hadamard_quantize), without
+ * writing the transform: x is [T tokens x F features], T % 16 == 0. */
+nvfp4_status nvfp4_hadamard_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
+                                 uint64_t sign_seed, float *amax_out, void *stream);
+
+/* 1D NVFP4 quantization of x [out->rows x out->cols] (row stride ld) into `out`
+ * (layout NVFP4_BLK_1x16, cols % 16 == 0) [P1 Caracteristicas; P2 Describir].
+ * amax_in: device pointer to the tensor amax to use, or NULL to compute it first (two passes).
+ * Writes out->codes, out->scales, *out->amax (= the amax used) and *out->s_dec. */
+nvfp4_status nvfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, const float *amax_in,
+                               nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
+                               void *stream);
+
+/* 2D NVFP4 quantization of a weight w [out->rows x out->cols] with one E4M3 scale per 16x16
+ * tile, round to nearest [P1 Metodologia: two-dimensional block scaling for weights].
+ * out: layout NVFP4_BLK_16x16, rows % 16 == cols % 16 == 0.  out_t (optional, may be NULL):
+ * the same quantized values transposed, [cols x rows], layout NVFP4_BLK_16x16 -- the dgrad
+ * operand.  Both share amax and s_dec values (out_t's amax/s_dec pointers are written too if
+ * they are non-NULL). */
+nvfp4_status nvfp4_quantize_2d(const void *w, nvfp4_dtype dt, int64_t ld, const float *amax_in,
+                               const nvfp4_tensor *out, const nvfp4_tensor *out_t, void *stream);
+
+/* Random Hadamard transform + transpose + 1D quantization of a wgrad operand
+ * [P1 Metodologia: random Hadamard transforms].  x is [T tokens x F features] (row stride ld);
+ * each 16-token chunk of each feature column is replaced by (1/4) H16 D x, with H16 the
+ * Sylvester Hadamard matrix and D = diag(d), d_j = -1 iff bit j of word 0 of
+ * Philox4x32-10(key = sign_seed, counter = 0) is set.  The result is written feature-major:
+ * out is [F x T] (out->rows = F, out->cols = T, layout NVFP4_BLK_1x16), so the token dimension
+ * is the contiguous K of the wgrad GEMM and each 16-token chunk is one NVFP4 block.
+ * amax_in: the amax of the TRANSFORMED tensor, or NULL to compute it. */
+nvfp4_status nvfp4_hadamard_quantize(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
+                                     const float *amax_in, nvfp4_round rnd, uint64_t seed,
+                                     const nvfp4_tensor *out, void *stream);
+
+/* Dequantize an NVFP4 tensor (1x16 or 16x16): y = fl(fl(v * scale_b) * s_dec) in fp32, stored
+ * as fp32 or rounded to nearest-even bf16.  y is [q->rows x q->cols], row stride ld. */
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dtype dt, int64_t ld,
+                              void *stream);
+
+/* NVFP4 x NVFP4 GEMM with fp32 accumulation [P2 Describir: weights, activations and gradients
+ * all in FP4]: C = A * B^T, A [M x K] (layout 1x16), B [N x K] (layout 1x16 or 16x16),
+ *   C[m,n] = s_dA * s_dB * sum_k (vA * sA) * (vB * sB),
+ * stored fp32 or bf16 (round to nearest even) into c [M x N] with row stride ldc.
+ * Requirements: a->cols == b->cols == K, K % 16 == 0; c need only be element-aligned. */
+nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
+                        int64_t ldc, void *stream);
+
+/* MXFP4 quantization (the comparison format of [P3 NVFP4 in pratica]): 32-element blocks along
+ * cols with an E8M0 scale 2^(floor(log2 amax_b) - 2) (byte = exponent + 127, clamped to
+ * [0, 254]; an all-zero block gets byte 127); codes E2M1 of x * 2^-exponent, RNE or SR as above.
+ * out: layout MXFP4_BLK_1x32, cols % 32 == 0; amax/s_dec are not used. */
+nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
+                               uint64_t seed, const nvfp4_tensor *out, void *stream);
+
+/* MXFP4 x MXFP4 GEMM, C = A * B^T with fp32 accumulation, both operands MXFP4_BLK_1x32. */
+nvfp4_status mxfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
+                        int64_t ldc, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,264 @@
+// hadamard.hip -- random Hadamard transform + transpose + NVFP4 quantization of the
+// weight-gradient operands, and the amax of the transformed tensor, for gfx950.
+//
+// [P1] "Entrenamiento de Modelos de Lenguaje con 4 Bits de Precision", Metodologia de
+// Entrenamiento: the recipe applies random Hadamard transforms.  Here: for every feature f and
+// 16-token chunk c of x [T x F], y = (1/4) H16 D x[16c..16c+15, f] with H16 the Sylvester
+// Hadamard matrix and D a random +-1 diagonal; y is quantized with 1x16 blocks along tokens and
+// written feature-major ([F x T]) so that tokens form the contiguous K of the wgrad GEMM.
+//
+// Thread mapping: a thread owns 8 consecutive features (one 16-byte bf16 load per token row)
+// and one 16-token chunk, so it holds the 16x8 input tile in registers and runs 8 independent
+// 16-point fast Walsh-Hadamard transforms.  A wave covers 8 feature groups (64 features, full
+// 128-byte rows on the read side) x 8 consecutive chunks (64 contiguous code bytes per feature
+// on the write side).
+
+#include "device_codecs.hpp"
+#include "host_util.hpp"
+
+namespace nvfp4 {
+
+constexpr int kRhtThreads = 256;
+constexpr int kFeatPerBlock = 64;                  // 8 feature groups of 8
+constexpr int kChunksPerBlock = kRhtThreads / 8;   // 32 chunks = 512 tokens
+
+// 16 token rows x 8 features of one thread, as raw 32-bit words (bf16: 4 per row, fp32: 8).
+template <typename T> struct Tile16x8;
+
+template <> struct Tile16x8<uint16_t> {
+    uint4 w[16];
+    __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[i] = *reinterpret_cast<const uint4*>(p + i * ld);
+    }
+    __device__ __forceinline__ float get(int i, int f) const {
+        const uint32_t v = f < 2 ? w[i].x : f < 4 ? w[i].y : f < 6 ? w[i].z : w[i].w;
+        return (f & 1) ? bf16_hi(v) : bf16_lo(v);
+    }
+};
+
+template <> struct Tile16x8<float> {
+    float4 a[16], b[16];
+    __device__ __forceinline__ void load(const float* p, int64_t ld) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            a[i] = reinterpret_cast<const float4*>(p + i * ld)[0];
+            b[i] = reinterpret_cast<const float4*>(p + i * ld)[1];
+        }
+    }
+    __device__ __forceinline__ float get(int i, int f) const {
+        const float4& v = f < 4 ? a[i] : b[i];
+        const int g = f & 3;
+        return g == 0 ? v.x : g == 1 ? v.y : g == 2 ? v.z : v.w;
+    }
+};
+
+// Sign mask: bit j set <=> d_j = -1.  Word 0 of Philox4x32-10(key = sign_seed, counter = 0).
+__device__ __forceinline__ uint32_t rht_sign_mask(uint64_t sign_seed) {
+    return philox4x32_10(0u, 0u, 0u, 0u, (uint32_t)sign_seed, (uint32_t)(sign_seed >> 32)).x & 0xFFFFu;
+}
+
+// In place: v <- (1/4) H16 D v with butterflies in the order h = 1, 2, 4, 8.
+__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
+#pragma unroll
+    for (int hs = 1; hs < 16; hs <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if ((i & hs) == 0) {
+                const float a = v[i], b = v[i + hs];
+                v[i] = a + b;
+                v[i + hs] = a - b;
+            }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
+}
+
+__global__ void k_fill_rht(float* p) { *p = 0.0f; }
+
+__global__ void k_scalars_rht(const float* src, float* amax_out, float* sdec_out) {
+    const float A = *src;
+    *amax_out = A;
+    *sdec_out = tensor_scales(A).s_dec;
+}
+
+struct RhtCoords {
+    int64_t f0;      // first feature of the thread
+    int64_t c;       // chunk index
+    bool valid;
+};
+
+__device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
+    RhtCoords rc;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    rc.f0 = (int64_t)blockIdx.x * kFeatPerBlock + (lane & 7) * 8;
+    rc.c = (int64_t)blockIdx.y * kChunksPerBlock + wave * 8 + (lane >> 3);
+    rc.valid = rc.f0 < F && rc.c * 16 < T;
+    return rc;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kRhtThreads)
+k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
+           float* amax_out) {
+    const RhtCoords rc = rht_coords(Tn, F);
+    const uint32_t mask = rht_sign_mask(sign_seed);
+    float m = 0.0f;
+    if (rc.valid) {
+        Tile16x8<T> tile;
+        tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
+            rht16(v, mask);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    __shared__ float part[kRhtThreads / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = part[0];
+#pragma unroll
+        for (int w = 1; w < kRhtThreads / 64; ++w) b = fmaxf(b, part[w]);
+        atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(b));
+    }
+}
+
+template <typename T, bool kSR>
+__global__ void __launch_bounds__(kRhtThreads)
+k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
+            const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
+            uint8_t* __restrict__ scales, float* amax_out, float* sdec_out) {
+    const float A = *amax_src;
+    const TensorScales ts = tensor_scales(A);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        *amax_out = A;
+        *sdec_out = ts.s_dec;
+    }
+    const RhtCoords rc = rht_coords(Tn, F);
+    if (!rc.valid) return;
+    const uint32_t mask = rht_sign_mask(sign_seed);
+    Tile16x8<T> tile;
+    tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int64_t feat = rc.f0 + f;
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
+        rht16(v, mask);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        uint32_t sb;
+        float enc;
+        block_scale(m, ts, sb, enc);
+        uint32_t lo = 0, hi = 0;
+        if constexpr (kSR) {
+            const uint64_t idx = (uint64_t)feat * (uint64_t)Tn + (uint64_t)rc.c * 16;
+            const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
+            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t ra = (e & 1) ? (a[e >> 1] >> 16) : (a[e >> 1] & 0xFFFFu);
+                const uint32_t rb = (e & 1) ? (b[e >> 1] >> 16) : (b[e >> 1] & 0xFFFFu);
+                const float za = v[e] * enc, zb = v[e + 8] * enc;
+                lo |= e2m1_sr_code2(za + za, ra) << (4 * e);
+                hi |= e2m1_sr_code2(zb + zb, rb) << (4 * e);
+            }
+        } else {
+            const float enc2 = enc + enc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                lo |= e2m1_rne_code2(v[e] * enc2) << (4 * e);
+                hi |= e2m1_rne_code2(v[e + 8] * enc2) << (4 * e);
+            }
+        }
+        if (feat < F) {
+            *reinterpret_cast<uint2*>(codes + feat * (Tn / 2) + rc.c * 8) = make_uint2(lo, hi);
+            scales[feat * (Tn / 16) + rc.c] = (uint8_t)sb;
+        }
+    }
+}
+
+static dim3 rht_grid(int64_t T, int64_t F) {
+    return dim3((unsigned)((F + kFeatPerBlock - 1) / kFeatPerBlock),
+                (unsigned)((T / 16 + kChunksPerBlock - 1) / kChunksPerBlock));
+}
+
+static nvfp4_status check_rht_input(const void* x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld) {
+    nvfp4_status s = check_input(x, dt, T, F, ld);
+    if (s) return s;
+    if (T % 16 != 0 || F % 8 != 0) return NVFP4_ERR_SHAPE;
+    if (T / 16 >= (1ll << 31) / kChunksPerBlock || F >= (1ll << 40)) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+static nvfp4_status launch_rht_amax(const void* x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
+                                    uint64_t sign_seed, float* dst, hipStream_t st) {
+    hipLaunchKernelGGL(k_fill_rht, dim3(1), dim3(1), 0, st, dst);
+    if (T > 0 && F > 0) {
+        if (dt == NVFP4_BF16)
+            hipLaunchKernelGGL(k_rht_amax<uint16_t>, rht_grid(T, F), dim3(kRhtThreads), 0, st,
+                               static_cast<const uint16_t*>(x), T, F, ld, sign_seed, dst);
+        else
+            hipLaunchKernelGGL(k_rht_amax<float>, rht_grid(T, F), dim3(kRhtThreads), 0, st,
+                               static_cast<const float*>(x), T, F, ld, sign_seed, dst);
+    }
+    return launch_status();
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" nvfp4_status nvfp4_hadamard_amax(const void* x, nvfp4_dtype dt, int64_t T, int64_t F,
+                                            int64_t ld, uint64_t sign_seed, float* amax_out,
+                                            void* stream) {
+    nvfp4_status s = check_rht_input(x, dt, T, F, ld);
+    if (s) return s;
+    if (!amax_out) return NVFP4_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(amax_out) & 3u) return NVFP4_ERR_ALIGN;
+    return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_out, as_stream(stream));
+}
+
+extern "C" nvfp4_status nvfp4_hadamard_quantize(const void* x, nvfp4_dtype dt, int64_t ld,
+                                                uint64_t sign_seed, const float* amax_in,
+                                                nvfp4_round rnd, uint64_t seed,
+                                                const nvfp4_tensor* out, void* stream) {
+    nvfp4_status s = check_q(out, NVFP4_BLK_1x16, true);
+    if (s) return s;
+    const int64_t F = out->rows, T = out->cols;
+    s = check_rht_input(x, dt, T, F, ld);
+    if (s) return s;
+    if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
+    hipStream_t st = as_stream(stream);
+    const float* src = amax_in;
+    if (!src) {
+        s = launch_rht_amax(x, dt, T, F, ld, sign_seed, out->amax, st);
+        if (s) return s;
+        src = out->amax;
+    }
+    if (T == 0 || F == 0) {
+        hipLaunchKernelGGL(k_scalars_rht, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
+        return launch_status();
+    }
+    const dim3 grid = rht_grid(T, F), block(kRhtThreads);
+#define NVFP4_RQ(TT, SRV)                                                                         \
+    hipLaunchKernelGGL((k_rht_quant<TT, SRV>), grid, block, 0, st, static_cast<const TT*>(x), T, F, \
+                       ld, sign_seed, src, seed, out->codes, out->scales, out->amax, out->s_dec)
+    if (dt == NVFP4_BF16) {
+        if (rnd == NVFP4_SR) NVFP4_RQ(uint16_t, true); else NVFP4_RQ(uint16_t, false);
+    } else {
+        if (rnd == NVFP4_SR) NVFP4_RQ(float, true); else NVFP4_RQ(float, false);
+    }
+#undef NVFP4_RQ
+    return launch_status();
+}

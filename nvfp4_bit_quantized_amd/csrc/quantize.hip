@@ -1,0 +1,538 @@
+// quantize.hip -- per-tensor amax, 1D/2D NVFP4 quantization, dequantization and the MXFP4
+// quantizer for gfx950.
+//
+// Citation keys: [P1] "Entrenamiento de Modelos de Lenguaje con 4 Bits de Precision";
+// [P2] "FP4 All the Way: Formacion totalmente cuantificada de LLM"; [P3] "I ricercatori di
+// Nvidia sbloccano il tutorial LLM a 8 bit che corrisponde alle prestazioni a 4 bit".
+//
+// All kernels here are HBM-bound streaming kernels.  Work is split into "groups" of 8
+// consecutive elements of a row: one 16-byte load for bf16 (two for fp32), one 32-bit store of
+// 8 packed codes.  Two adjacent lanes hold one 16-element NVFP4 block and exchange their partial
+// amax with a single DPP lane swap.  Each thread handles UNROLL groups whose loads are issued
+// before any arithmetic, to keep enough bytes in flight.
+
+#include "device_codecs.hpp"
+#include "host_util.hpp"
+
+namespace nvfp4 {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+// 8 input elements of one group as fp32.
+template <typename T> struct Group8;
+
+template <> struct Group8<uint16_t> {   // bf16
+    static __device__ __forceinline__ void load(const uint16_t* p, float* y) {
+        uint4 v = *reinterpret_cast<const uint4*>(p);
+        y[0] = bf16_lo(v.x); y[1] = bf16_hi(v.x); y[2] = bf16_lo(v.y); y[3] = bf16_hi(v.y);
+        y[4] = bf16_lo(v.z); y[5] = bf16_hi(v.z); y[6] = bf16_lo(v.w); y[7] = bf16_hi(v.w);
+    }
+};
+
+template <> struct Group8<float> {
+    static __device__ __forceinline__ void load(const float* p, float* y) {
+        float4 a = reinterpret_cast<const float4*>(p)[0];
+        float4 b = reinterpret_cast<const float4*>(p)[1];
+        y[0] = a.x; y[1] = a.y; y[2] = a.z; y[3] = a.w;
+        y[4] = b.x; y[5] = b.y; y[6] = b.z; y[7] = b.w;
+    }
+};
+
+__global__ void k_fill_f32(float* p, float v) { *p = v; }
+
+// Writes amax/s_dec for an empty tensor (A taken from src, 0 if src is NULL).
+__global__ void k_tensor_scalars(const float* src, float* amax_out, float* sdec_out) {
+    float A = src ? *src : 0.0f;
+    TensorScales ts = tensor_scales(A);
+    if (amax_out) *amax_out = A;
+    if (sdec_out) *sdec_out = ts.s_dec;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// ---- per-tensor amax [P3 Come funziona NVFP4?] ------------------------------------------------
+// Grid-stride over groups; one device-scope atomicMax of the float bits per workgroup (the
+// values are non-negative, so their IEEE bit patterns order like the floats).
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+k_amax(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, float* amax_out) {
+    float m = 0.0f;
+    const uint32_t stride = gridDim.x * kThreads * kUnroll;
+    for (uint32_t base = blockIdx.x * kThreads * kUnroll + threadIdx.x; base < groups;
+         base += stride) {
+        float y[kUnroll][8];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            uint32_t g = base + u * kThreads;
+            if (g < groups) {
+                uint32_t row = fastdiv(g, gpr);
+                uint32_t cg = g - row * gpr.d;
+                Group8<T>::load(x + (int64_t)row * ld + cg * 8, y[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[u][e] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[u][e]));
+    }
+    m = wave_max(m);
+    __shared__ float part[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = part[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, part[w]);
+        atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(b));
+    }
+}
+
+static int amax_grid(uint32_t groups) {
+    int64_t need = ((int64_t)groups + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+    int64_t cap = 256 * 4;                       // 4 workgroups per CU on 256 CUs
+    return (int)(need < 1 ? 1 : (need < cap ? need : cap));
+}
+
+// ---- 1D quantization [P1 Caracteristicas; P2 Describir] ---------------------------------------
+template <typename T, bool kSR>
+__global__ void __launch_bounds__(kThreads)
+k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, uint32_t cols,
+          const float* __restrict__ amax_src, uint64_t seed, uint32_t* __restrict__ codes,
+          uint8_t* __restrict__ scales, float* amax_out, float* sdec_out) {
+    const float A = *amax_src;
+    const TensorScales ts = tensor_scales(A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *amax_out = A;
+        *sdec_out = ts.s_dec;
+    }
+    const uint32_t base = blockIdx.x * kThreads * kUnroll + threadIdx.x;
+    float y[kUnroll][8];
+    uint32_t row[kUnroll], cg[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        uint32_t g = base + u * kThreads;
+        row[u] = 0; cg[u] = 0;
+        if (g < groups) {
+            row[u] = fastdiv(g, gpr);
+            cg[u] = g - row[u] * gpr.d;
+            Group8<T>::load(x + (int64_t)row[u] * ld + cg[u] * 8, y[u]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[u][e] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t g = base + u * kThreads;
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[u][e]));
+        m = fmaxf(m, swap_adjacent(m));          // amax of the 16-element block
+        uint32_t sb;
+        float enc;
+        block_scale(m, ts, sb, enc);
+        uint32_t packed = 0;
+        if constexpr (kSR) {
+            const uint64_t idx8 = (uint64_t)row[u] * cols + cg[u] * 8;
+            const u32x4 w = sr_words(seed, idx8);
+            const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float z = y[u][e] * enc;
+                uint32_t r16 = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+                packed |= e2m1_sr_code2(z + z, r16) << (4 * e);
+            }
+        } else {
+            const float enc2 = enc + enc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) packed |= e2m1_rne_code2(y[u][e] * enc2) << (4 * e);
+        }
+        if (g < groups) {
+            codes[g] = packed;                   // groups are dense in the code array
+            if ((g & 1u) == 0) scales[g >> 1] = (uint8_t)sb;
+        }
+    }
+}
+
+// ---- 2D quantization of weights [P1 Metodologia: two-dimensional block scaling] ---------------
+// A wave covers 4 tiles of 16x16; lane (t = lane/16, r = lane%16) holds row r of tile t (16
+// elements).  The tile amax is a max over the 16 lanes of the tile.  The transposed copy is
+// built by staging the tile's codes in LDS, one byte per element.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols, uint32_t tiles,
+          FastDiv tiles_per_row, const float* __restrict__ amax_src,
+          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+          uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
+          float* amax_out, float* sdec_out, float* amax_out_t, float* sdec_out_t) {
+    __shared__ uint32_t stage[kThreads / 64][4][16][5];    // [wave][tile][row][16 bytes + pad]
+    const float A = *amax_src;
+    const TensorScales ts = tensor_scales(A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *amax_out = A;
+        *sdec_out = ts.s_dec;
+        if (amax_out_t) *amax_out_t = A;
+        if (sdec_out_t) *sdec_out_t = ts.s_dec;
+    }
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = lane >> 4, r = lane & 15;
+    const uint32_t tile = (blockIdx.x * (kThreads / 64) + wv) * 4 + t;
+    const bool valid = tile < tiles;
+    uint32_t ti = 0, tj = 0;
+    float y[16];
+    if (valid) {
+        ti = fastdiv(tile, tiles_per_row);
+        tj = tile - ti * tiles_per_row.d;
+        const T* p = w + (int64_t)(ti * 16 + r) * ld + tj * 16;
+        Group8<T>::load(p, y);
+        Group8<T>::load(p + 8, y + 8);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) y[e] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(y[e]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    uint32_t sb;
+    float enc;
+    block_scale(m, ts, sb, enc);
+    const float enc2 = enc + enc;
+    uint32_t c8[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c8[e] = e2m1_rne_code2(y[e] * enc2);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        lo |= c8[e] << (4 * e);
+        hi |= c8[e + 8] << (4 * e);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        stage[wv][t][r][q] = c8[4 * q] | (c8[4 * q + 1] << 8) | (c8[4 * q + 2] << 16) |
+                             (c8[4 * q + 3] << 24);
+    if (valid) {
+        *reinterpret_cast<uint2*>(codes + (int64_t)(ti * 16 + r) * (cols / 2) + tj * 8) =
+            make_uint2(lo, hi);
+        if (r == 0) scales[(int64_t)ti * tiles_per_row.d + tj] = (uint8_t)sb;
+    }
+    __syncthreads();
+    if (valid && codes_t) {
+        // column r of the tile becomes row (16 tj + r) of the transposed matrix
+        const uint8_t* st = reinterpret_cast<const uint8_t*>(&stage[wv][t][0][0]);
+        uint32_t tlo = 0, thi = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            tlo |= (uint32_t)st[e * 20 + r] << (4 * e);
+            thi |= (uint32_t)st[(e + 8) * 20 + r] << (4 * e);
+        }
+        *reinterpret_cast<uint2*>(codes_t + (int64_t)(tj * 16 + r) * (rows / 2) + ti * 8) =
+            make_uint2(tlo, thi);
+        if (r == 0) scales_t[(int64_t)tj * (rows / 16) + ti] = (uint8_t)sb;
+    }
+}
+
+// ---- dequantization -------------------------------------------------------------------------
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+    uint32_t m = c & 7u;
+    float mag = m < 2 ? 0.5f * (float)m : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
+    return (c & 8u) ? -mag : mag;
+}
+
+template <bool kBF16Out>
+__global__ void __launch_bounds__(kThreads)
+k_dequant(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales, int layout,
+          const float* __restrict__ sdec_src, uint32_t groups, FastDiv gpr, uint32_t cols,
+          void* __restrict__ out, int64_t ld) {
+    const float sdec = layout == MXFP4_BLK_1x32 ? 1.0f : *sdec_src;
+    const uint32_t base = blockIdx.x * kThreads * kUnroll + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t g = base + u * kThreads;
+        if (g >= groups) break;
+        const uint32_t row = fastdiv(g, gpr), cg = g - row * gpr.d;
+        const uint32_t c = codes[g];
+        float v[8];
+        if (layout == MXFP4_BLK_1x32) {
+            const int e = (int)scales[(int64_t)row * (cols / 32) + cg / 4] - 127;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_amdgcn_ldexpf(e2m1_decode(c >> (4 * i)), e);
+        } else {
+            const uint32_t sb = layout == NVFP4_BLK_16x16
+                                    ? scales[(int64_t)(row / 16) * (cols / 16) + cg / 2]
+                                    : scales[(int64_t)row * (cols / 16) + cg / 2];
+            const float s = e4m3_decode(sb);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = (e2m1_decode(c >> (4 * i)) * s) * sdec;
+        }
+        if constexpr (kBF16Out) {
+            uint4 o;
+            o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+            o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+            o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+            o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)row * ld + cg * 8) = o;
+        } else {
+            float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)row * ld + cg * 8);
+            o[0] = make_float4(v[0], v[1], v[2], v[3]);
+            o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
+    }
+}
+
+// ---- MXFP4 quantization (comparison format, [P3 NVFP4 in pratica]) -----------------------------
+// Four adjacent lanes hold one 32-element block.  E8M0 exponent = floor(log2 amax_b) - 2.
+template <typename T, bool kSR>
+__global__ void __launch_bounds__(kThreads)
+k_mx_quant(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, uint32_t cols,
+           uint64_t seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const uint32_t base = blockIdx.x * kThreads * kUnroll + threadIdx.x;
+    float y[kUnroll][8];
+    uint32_t row[kUnroll], cg[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        uint32_t g = base + u * kThreads;
+        row[u] = 0; cg[u] = 0;
+        if (g < groups) {
+            row[u] = fastdiv(g, gpr);
+            cg[u] = g - row[u] * gpr.d;
+            Group8<T>::load(x + (int64_t)row[u] * ld + cg[u] * 8, y[u]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[u][e] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t g = base + u * kThreads;
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[u][e]));
+        m = fmaxf(m, swap_adjacent(m));
+        m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));
+        int e8 = 0;
+        if (m > 0.0f) {
+            e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
+            e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
+        }
+        uint32_t packed = 0;
+        if constexpr (kSR) {
+            const uint64_t idx8 = (uint64_t)row[u] * cols + cg[u] * 8;
+            const u32x4 w = sr_words(seed, idx8);
+            const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float z = __builtin_amdgcn_ldexpf(y[u][e], -e8);
+                uint32_t r16 = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+                packed |= e2m1_sr_code2(z + z, r16) << (4 * e);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                packed |= e2m1_rne_code2(__builtin_amdgcn_ldexpf(y[u][e], 1 - e8)) << (4 * e);
+        }
+        if (g < groups) {
+            codes[g] = packed;
+            if ((g & 3u) == 0) scales[g >> 2] = (uint8_t)(e8 + 127);
+        }
+    }
+}
+
+static int stream_grid(uint32_t groups) {
+    int64_t n = ((int64_t)groups + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+    return (int)(n < 1 ? 1 : n);
+}
+
+// Launch the amax pass for a dense [rows x cols] input into *dst (zeroed first).
+static nvfp4_status launch_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                int64_t ld, float* dst, hipStream_t st) {
+    hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, dst, 0.0f);
+    const int64_t g64 = rows * (cols / 8);
+    if (g64 > 0) {
+        const uint32_t groups = (uint32_t)g64;
+        const FastDiv gpr = make_fastdiv((uint32_t)(cols / 8));
+        const dim3 grid(amax_grid(groups));
+        if (dt == NVFP4_BF16)
+            hipLaunchKernelGGL(k_amax<uint16_t>, grid, dim3(kThreads), 0, st,
+                               static_cast<const uint16_t*>(x), ld, groups, gpr, dst);
+        else
+            hipLaunchKernelGGL(k_amax<float>, grid, dim3(kThreads), 0, st,
+                               static_cast<const float*>(x), ld, groups, gpr, dst);
+    }
+    return launch_status();
+}
+
+static bool too_big(int64_t rows, int64_t cols) {
+    return rows * (cols / 8) >= (int64_t(1) << 31);
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" const char* nvfp4_status_string(nvfp4_status s) {
+    switch (s) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_ERR_NULL: return "a required pointer is NULL";
+        case NVFP4_ERR_SHAPE: return "invalid or mismatched shape";
+        case NVFP4_ERR_DTYPE: return "unknown dtype or rounding mode";
+        case NVFP4_ERR_ALIGN: return "pointer or row stride not 16-byte aligned";
+        case NVFP4_ERR_LAYOUT: return "tensor layout not allowed for this call";
+        case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+extern "C" nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                   int64_t ld, float* amax_out, void* stream) {
+    nvfp4_status s = check_input(x, dt, rows, cols, ld);
+    if (s) return s;
+    if (!amax_out) return NVFP4_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(amax_out) & 3u) return NVFP4_ERR_ALIGN;
+    if (cols % 8 != 0) return NVFP4_ERR_SHAPE;
+    if (too_big(rows, cols)) return NVFP4_ERR_SHAPE;
+    return launch_amax(x, dt, rows, cols, ld, amax_out, as_stream(stream));
+}
+
+extern "C" nvfp4_status nvfp4_quantize_1d(const void* x, nvfp4_dtype dt, int64_t ld,
+                                          const float* amax_in, nvfp4_round rnd, uint64_t seed,
+                                          const nvfp4_tensor* out, void* stream) {
+    nvfp4_status s = check_q(out, NVFP4_BLK_1x16, true);
+    if (s) return s;
+    s = check_input(x, dt, out->rows, out->cols, ld);
+    if (s) return s;
+    if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
+    if (too_big(out->rows, out->cols)) return NVFP4_ERR_SHAPE;
+    hipStream_t st = as_stream(stream);
+    const float* src = amax_in;
+    if (!src) {
+        s = launch_amax(x, dt, out->rows, out->cols, ld, out->amax, st);
+        if (s) return s;
+        src = out->amax;
+    }
+    const uint32_t groups = (uint32_t)(out->rows * (out->cols / 8));
+    if (groups == 0) {
+        hipLaunchKernelGGL(k_tensor_scalars, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
+        return launch_status();
+    }
+    const FastDiv gpr = make_fastdiv((uint32_t)(out->cols / 8));
+    const dim3 grid(stream_grid(groups)), block(kThreads);
+    uint32_t* codes = reinterpret_cast<uint32_t*>(out->codes);
+    const uint32_t cols = (uint32_t)out->cols;
+#define NVFP4_Q1(T, SRV)                                                                         \
+    hipLaunchKernelGGL((k_quant1d<T, SRV>), grid, block, 0, st, static_cast<const T*>(x), ld,     \
+                       groups, gpr, cols, src, seed, codes, out->scales, out->amax, out->s_dec)
+    if (dt == NVFP4_BF16) {
+        if (rnd == NVFP4_SR) NVFP4_Q1(uint16_t, true); else NVFP4_Q1(uint16_t, false);
+    } else {
+        if (rnd == NVFP4_SR) NVFP4_Q1(float, true); else NVFP4_Q1(float, false);
+    }
+#undef NVFP4_Q1
+    return launch_status();
+}
+
+extern "C" nvfp4_status nvfp4_quantize_2d(const void* w, nvfp4_dtype dt, int64_t ld,
+                                          const float* amax_in, const nvfp4_tensor* out,
+                                          const nvfp4_tensor* out_t, void* stream) {
+    nvfp4_status s = check_q(out, NVFP4_BLK_16x16, true);
+    if (s) return s;
+    if (out_t) {
+        s = check_q(out_t, NVFP4_BLK_16x16, false);
+        if (s) return s;
+        if (out_t->rows != out->cols || out_t->cols != out->rows) return NVFP4_ERR_SHAPE;
+    }
+    s = check_input(w, dt, out->rows, out->cols, ld);
+    if (s) return s;
+    if (too_big(out->rows, out->cols)) return NVFP4_ERR_SHAPE;
+    hipStream_t st = as_stream(stream);
+    const float* src = amax_in;
+    if (!src) {
+        s = launch_amax(w, dt, out->rows, out->cols, ld, out->amax, st);
+        if (s) return s;
+        src = out->amax;
+    }
+    const uint32_t tiles = (uint32_t)((out->rows / 16) * (out->cols / 16));
+    float* amax_t = out_t ? out_t->amax : nullptr;
+    float* sdec_t = out_t ? out_t->s_dec : nullptr;
+    if (tiles == 0) {
+        hipLaunchKernelGGL(k_tensor_scalars, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
+        if (out_t) hipLaunchKernelGGL(k_tensor_scalars, dim3(1), dim3(1), 0, st, src, amax_t, sdec_t);
+        return launch_status();
+    }
+    const FastDiv tpr = make_fastdiv((uint32_t)(out->cols / 16));
+    const int tiles_per_block = (kThreads / 64) * 4;
+    const dim3 grid((tiles + tiles_per_block - 1) / tiles_per_block), block(kThreads);
+    uint8_t* ct = out_t ? out_t->codes : nullptr;
+    uint8_t* sct = out_t ? out_t->scales : nullptr;
+    const uint32_t rows = (uint32_t)out->rows, cols = (uint32_t)out->cols;
+    if (dt == NVFP4_BF16)
+        hipLaunchKernelGGL(k_quant2d<uint16_t>, grid, block, 0, st, static_cast<const uint16_t*>(w),
+                           ld, rows, cols, tiles, tpr, src, out->codes, out->scales, ct, sct,
+                           out->amax, out->s_dec, amax_t, sdec_t);
+    else
+        hipLaunchKernelGGL(k_quant2d<float>, grid, block, 0, st, static_cast<const float*>(w), ld,
+                           rows, cols, tiles, tpr, src, out->codes, out->scales, ct, sct,
+                           out->amax, out->s_dec, amax_t, sdec_t);
+    return launch_status();
+}
+
+extern "C" nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, nvfp4_dtype dt,
+                                         int64_t ld, void* stream) {
+    if (!q) return NVFP4_ERR_NULL;
+    nvfp4_status s = check_q(q, q->layout, q->layout != MXFP4_BLK_1x32);
+    if (s) return s;
+    if (q->layout != NVFP4_BLK_1x16 && q->layout != NVFP4_BLK_16x16 && q->layout != MXFP4_BLK_1x32)
+        return NVFP4_ERR_LAYOUT;
+    s = check_input(y, dt, q->rows, q->cols, ld);
+    if (s) return s;
+    if (too_big(q->rows, q->cols)) return NVFP4_ERR_SHAPE;
+    const uint32_t groups = (uint32_t)(q->rows * (q->cols / 8));
+    if (groups == 0) return NVFP4_OK;
+    const FastDiv gpr = make_fastdiv((uint32_t)(q->cols / 8));
+    const dim3 grid(stream_grid(groups)), block(kThreads);
+    hipStream_t st = as_stream(stream);
+    const uint32_t* codes = reinterpret_cast<const uint32_t*>(q->codes);
+    if (dt == NVFP4_BF16)
+        hipLaunchKernelGGL(k_dequant<true>, grid, block, 0, st, codes, q->scales, (int)q->layout,
+                           q->s_dec, groups, gpr, (uint32_t)q->cols, y, ld);
+    else
+        hipLaunchKernelGGL(k_dequant<false>, grid, block, 0, st, codes, q->scales, (int)q->layout,
+                           q->s_dec, groups, gpr, (uint32_t)q->cols, y, ld);
+    return launch_status();
+}
+
+extern "C" nvfp4_status mxfp4_quantize_1d(const void* x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
+                                          uint64_t seed, const nvfp4_tensor* out, void* stream) {
+    nvfp4_status s = check_q(out, MXFP4_BLK_1x32, false);
+    if (s) return s;
+    s = check_input(x, dt, out->rows, out->cols, ld);
+    if (s) return s;
+    if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
+    if (too_big(out->rows, out->cols)) return NVFP4_ERR_SHAPE;
+    const uint32_t groups = (uint32_t)(out->rows * (out->cols / 8));
+    if (groups == 0) return NVFP4_OK;
+    const FastDiv gpr = make_fastdiv((uint32_t)(out->cols / 8));
+    const dim3 grid(stream_grid(groups)), block(kThreads);
+    hipStream_t st = as_stream(stream);
+    uint32_t* codes = reinterpret_cast<uint32_t*>(out->codes);
+    const uint32_t cols = (uint32_t)out->cols;
+#define NVFP4_MXQ(T, SRV)                                                                        \
+    hipLaunchKernelGGL((k_mx_quant<T, SRV>), grid, block, 0, st, static_cast<const T*>(x), ld,    \
+                       groups, gpr, cols, seed, codes, out->scales)
+    if (dt == NVFP4_BF16) {
+        if (rnd == NVFP4_SR) NVFP4_MXQ(uint16_t, true); else NVFP4_MXQ(uint16_t, false);
+    } else {
+        if (rnd == NVFP4_SR) NVFP4_MXQ(float, true); else NVFP4_MXQ(float, false);
+    }
+#undef NVFP4_MXQ
+    return launch_status();
+}

@@ -1,0 +1,103 @@
+"""C-ABI contract checks that run without a GPU: the library loads, exports every function that
+include/nvfp4.h declares, and rejects bad arguments before anything is enqueued (only argument
+combinations that fail validation are passed, so no kernel is ever launched here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import nvfp4_bit_quantized_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:nvfp4|mxfp4)_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.LIB_PATH):
+        pytest.skip("libnvfp4.so not built")
+    return nv.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(nv.SYMBOLS)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.nvfp4_status_string(s)
+    assert L.nvfp4_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _q(rows, cols, layout=nv.BLK_1x16, codes=FAKE, scales=FAKE, amax=FAKE, sdec=FAKE, reserved=0):
+    return nv.NvTensor(codes, scales, amax, sdec, rows, cols, layout, reserved)
+
+
+def test_quantize_validation(L):
+    q = _q(8, 32)
+    assert L.nvfp4_quantize_1d(None, nv.BF16, 32, None, nv.RNE, 0, C.byref(q), None) == nv.ERR_NULL
+    assert L.nvfp4_quantize_1d(FAKE, 7, 32, None, nv.RNE, 0, C.byref(q), None) == nv.ERR_DTYPE
+    assert L.nvfp4_quantize_1d(FAKE, nv.BF16, 32, None, 5, 0, C.byref(q), None) == nv.ERR_DTYPE
+    assert L.nvfp4_quantize_1d(FAKE, nv.BF16, 16, None, nv.RNE, 0, C.byref(q), None) == nv.ERR_SHAPE
+    assert L.nvfp4_quantize_1d(FAKE + 2, nv.BF16, 32, None, nv.RNE, 0, C.byref(q), None) == nv.ERR_ALIGN
+    assert L.nvfp4_quantize_1d(FAKE, nv.BF16, 36, None, nv.RNE, 0, C.byref(q), None) == nv.ERR_ALIGN
+    bad = _q(8, 24)
+    assert L.nvfp4_quantize_1d(FAKE, nv.BF16, 32, None, nv.RNE, 0, C.byref(bad), None) == nv.ERR_SHAPE
+    wrong = _q(8, 32, layout=nv.BLK_16x16)
+    assert L.nvfp4_quantize_1d(FAKE, nv.BF16, 32, None, nv.RNE, 0, C.byref(wrong), None) == nv.ERR_LAYOUT
+    noamax = _q(8, 32, amax=None)
+    assert L.nvfp4_quantize_1d(FAKE, nv.BF16, 32, None, nv.RNE, 0, C.byref(noamax), None) == nv.ERR_NULL
+    assert L.nvfp4_quantize_1d(FAKE, nv.BF16, 32, None, nv.RNE, 0, None, None) == nv.ERR_NULL
+    res = _q(8, 32, reserved=1)
+    assert L.nvfp4_quantize_1d(FAKE, nv.BF16, 32, None, nv.RNE, 0, C.byref(res), None) == nv.ERR_LAYOUT
+
+
+def test_quantize_2d_and_hadamard_validation(L):
+    w = _q(24, 32, layout=nv.BLK_16x16)          # rows not a multiple of 16
+    assert L.nvfp4_quantize_2d(FAKE, nv.BF16, 32, None, C.byref(w), None, None) == nv.ERR_SHAPE
+    w = _q(32, 48, layout=nv.BLK_16x16)
+    wt = _q(32, 48, layout=nv.BLK_16x16)         # transposed copy must be [48 x 32]
+    assert L.nvfp4_quantize_2d(FAKE, nv.BF16, 48, None, C.byref(w), C.byref(wt), None) == nv.ERR_SHAPE
+    h = _q(12, 40)                               # F=12 features (not a multiple of 8), T=40 (not %16)
+    assert L.nvfp4_hadamard_quantize(FAKE, nv.BF16, 16, 1, None, nv.RNE, 0, C.byref(h), None) == nv.ERR_SHAPE
+    assert L.nvfp4_hadamard_amax(FAKE, nv.BF16, 40, 16, 16, 1, FAKE, None) == nv.ERR_SHAPE
+    assert L.nvfp4_hadamard_amax(FAKE, nv.BF16, 32, 16, 16, 1, None, None) == nv.ERR_NULL
+    assert L.nvfp4_amax(FAKE, nv.BF16, 4, 16, 16, FAKE + 1, None) == nv.ERR_ALIGN
+
+
+def test_gemm_validation(L):
+    a, b = _q(64, 64), _q(32, 48)
+    assert L.nvfp4_gemm(C.byref(a), C.byref(b), FAKE, nv.F32, 32, None) == nv.ERR_SHAPE
+    b = _q(32, 64, layout=nv.MX_1x32)
+    assert L.nvfp4_gemm(C.byref(a), C.byref(b), FAKE, nv.F32, 32, None) == nv.ERR_LAYOUT
+    b = _q(32, 64)
+    assert L.nvfp4_gemm(C.byref(a), C.byref(b), FAKE, nv.F32, 16, None) == nv.ERR_SHAPE
+    assert L.nvfp4_gemm(C.byref(a), C.byref(b), None, nv.F32, 32, None) == nv.ERR_NULL
+    assert L.nvfp4_gemm(C.byref(a), C.byref(b), FAKE, 9, 32, None) == nv.ERR_DTYPE
+    nos = _q(32, 64, sdec=None)
+    assert L.nvfp4_gemm(C.byref(a), C.byref(nos), FAKE, nv.F32, 32, None) == nv.ERR_NULL
+    mxa, mxb = _q(64, 48, layout=nv.MX_1x32), _q(32, 48, layout=nv.MX_1x32)
+    assert L.mxfp4_gemm(C.byref(mxa), C.byref(mxb), FAKE, nv.F32, 32, None) == nv.ERR_SHAPE
+    assert L.mxfp4_quantize_1d(FAKE, nv.BF16, 48, nv.RNE, 0, C.byref(mxa), None) == nv.ERR_SHAPE
+
+
+def test_dequantize_validation(L):
+    q = _q(16, 32)
+    assert L.nvfp4_dequantize(C.byref(q), None, nv.F32, 32, None) == nv.ERR_NULL
+    assert L.nvfp4_dequantize(C.byref(q), FAKE, nv.F32, 8, None) == nv.ERR_SHAPE
+    assert L.nvfp4_dequantize(None, FAKE, nv.F32, 32, None) == nv.ERR_NULL
+    bad = _q(16, 32, layout=7)
+    assert L.nvfp4_dequantize(C.byref(bad), FAKE, nv.F32, 32, None) == nv.ERR_LAYOUT
