@@ -36,74 +36,78 @@ __device__ __forceinline__ TensorScales tensor_scales(float A) {
 
 // ---- E4M3 (OCP E4M3FN), non-negative operands -----------------------------------------------
 // Round to nearest even with saturation at 448 (0x7E); values below 2^-6 use the subnormal
-// quantum 2^-9.
+// quantum 2^-9.  Branch-free: both candidate encodings are formed and one is selected.
 __device__ __forceinline__ uint32_t e4m3_encode(float t) {
-    if (t >= 448.0f) return 0x7Eu;
-    if (t < 0x1p-6f) return (uint32_t)__builtin_rintf(t * 512.0f);
+    const uint32_t sub = (uint32_t)__builtin_rintf(t * 512.0f);     // t < 2^-6: multiples of 2^-9
     uint32_t b = __float_as_uint(t);
-    b += 0x7FFFFu + ((b >> 20) & 1u);          // round the mantissa to 3 bits, ties to even
-    uint32_t r = (b >> 20) - 960u;             // re-bias the exponent from 127 to 7
-    return r < 0x7Eu ? r : 0x7Eu;
+    b += 0x7FFFFu + ((b >> 20) & 1u);                               // mantissa to 3 bits, RNE
+    uint32_t nrm = (b >> 20) - 960u;                                // exponent bias 127 -> 7
+    nrm = nrm < 0x7Eu ? nrm : 0x7Eu;
+    return t < 0x1p-6f ? sub : (t >= 448.0f ? 0x7Eu : nrm);
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
-    uint32_t e = b >> 3;
-    return e == 0 ? (float)(b & 7u) * 0x1p-9f : __uint_as_float((b + 960u) << 20);
+    const float sub = (float)(b & 7u) * 0x1p-9f;
+    const float nrm = __uint_as_float((b + 960u) << 20);
+    return b < 8u ? sub : nrm;
 }
 
 // Block step: scale byte and the element encode factor s_enc / scale (0 for a zero scale).
+// The division is a single correctly rounded fp32 division.
 __device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts,
                                             uint32_t& scale_byte, float& enc) {
-    float t = amax_b * ts.k1;
+    const float t = amax_b * ts.k1;
     scale_byte = e4m3_encode(t);
-    enc = scale_byte == 0 ? 0.0f : ts.s_enc / e4m3_decode(scale_byte);
+    const float d = scale_byte == 0 ? 1.0f : e4m3_decode(scale_byte);
+    const float e = ts.s_enc / d;
+    enc = scale_byte == 0 ? 0.0f : e;
 }
 
 // ---- E2M1 [P1 Caracteristicas: 1 sign, 2 exponent, 1 mantissa bit] --------------------------
-// Magnitude index from a grid value held as 2*r in {0,1,2,3,4,6,8,12}: n<=4 -> n, 6->5, 8->6,
-// 12->7, i.e. min(n, n/4 + 4).
-__device__ __forceinline__ uint32_t e2m1_index_from_twice(uint32_t n) {
-    uint32_t q = (n >> 2) + 4u;
-    return n < q ? n : q;
-}
 
-// Round-to-nearest-even of z2 = 2*z onto the doubled grid {0,1,2,3,4,6,8,12} (saturating),
-// returning the 4-bit code of z (sign kept, so -0 and small negatives give 0x8).
-// The quantum of the doubled grid is 1 below 4, 2 in [4,8) and 4 in [8,12]; adding and
-// removing 2^(E+22) with E = max(exponent(z2), 1) rounds at exactly that quantum.
-__device__ __forceinline__ uint32_t e2m1_rne_code2(float z2) {
-    uint32_t sign = (__float_as_uint(z2) >> 28) & 8u;
-    float a = __builtin_fminf(__builtin_fabsf(z2), 12.0f);
-    uint32_t e = __float_as_uint(a) & 0x7F800000u;
-    e = e > 0x40000000u ? e : 0x40000000u;
-    float C = __uint_as_float(e + (22u << 23));
-    float r = (a + C) - C;
-    return sign | e2m1_index_from_twice((uint32_t)r);
-}
-
-// Stochastic rounding of z2 = 2*z [P2 Describir: stochastic rounding in the backward pass]
-// (callers form z2 as z + z from the rounded product z, so the doubling is exact even for
-// subnormal z):
-// with lo <= |z| < hi the neighbouring grid values, round up iff r16 < 65536 * (|z|-lo)/(hi-lo).
-// In the doubled grid the neighbours of a2 = |z2| are lo2 = a2 truncated to its quantum q
-// (q = 1 below 4, else the exponent's power / 2), hi2 = lo2 + q, and the comparison
-// r16 < (a2 - lo2) * 65536 / q is exact in fp32.  |z| >= 6 saturates without randomness.
+// Stochastic rounding of one element [P2 Describir: stochastic rounding in the backward pass]:
+// with lo <= |z| < hi the neighbouring grid values, round up iff r16 < 65536 (|z|-lo)/(hi-lo);
+// |z| >= 6 saturates; sign kept.  Works on z2 = 2z (callers form it as z + z, exact) whose grid
+// 0,1,2,3,4,6,8,12 has spacing 1 below 4, 2 in [4,8) and 4 above: scaling a2 = |z2| by
+// s = 1, 1/2 or 1/4 puts every region on an integer grid, so (|z|-lo)/(hi-lo) = fract(a2 s)
+// and the rounded value is floor(a2 s) + up, all exact in fp32.  The magnitude code is that
+// integer plus the region's offset (0, 2, 4), clamped to 7 (which also saturates a2 >= 12).
 __device__ __forceinline__ uint32_t e2m1_sr_code2(float z2, uint32_t r16) {
-    uint32_t sign = (__float_as_uint(z2) >> 28) & 8u;
-    float a = __builtin_fabsf(z2);
-    uint32_t idx;
-    if (a >= 12.0f) {
-        idx = 7u;
-    } else {
-        uint32_t ab = __float_as_uint(a);
-        // quantum q: 1 for a < 4, else 2^(E-1) for a in [2^E, 2^(E+1))
-        float q = a < 4.0f ? 1.0f : __uint_as_float((ab & 0x7F800000u) - (1u << 23));
-        float lo = a < 4.0f ? __builtin_floorf(a) : __uint_as_float(ab & 0xFFC00000u);
-        float frac = (a - lo) * (65536.0f / q);          // exact: q is a power of two
-        float r = ((float)r16 < frac) ? lo + q : lo;
-        idx = e2m1_index_from_twice((uint32_t)r);
+    const uint32_t zb = __float_as_uint(z2);
+    const uint32_t sign = (zb >> 28) & 8u;
+    const float a = __uint_as_float(zb & 0x7FFFFFFFu);
+    const uint32_t c4 = a >= 4.0f, c8 = a >= 8.0f;
+    const float s = c8 ? 0.25f : (c4 ? 0.5f : 1.0f);
+    const float as = a * s;
+    const float fl = __builtin_floorf(as);
+    const float f = as - fl;
+    const uint32_t up = (float)r16 < f * 65536.0f;
+    const uint32_t idx = (uint32_t)fl + up + 2u * (c4 + c8);
+    return sign | (idx < 7u ? idx : 7u);
+}
+
+// Eight codes: element e takes the 16-bit half (e & 1) of w[e >> 1] (low half first), packed
+// element 2j -> low nibble of byte j.  z2[e] = 2 z[e].
+__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float* z2, const uint32_t* w) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t r16 = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+        packed |= e2m1_sr_code2(z2[e], r16) << (4 * e);
     }
-    return sign | idx;
+    return packed;
+}
+
+// Eight E2M1 codes of z[0..7] rounded to nearest even (ties to the even code, saturating at 6,
+// sign kept), packed element 2j -> low nibble of byte j.  gfx950's v_cvt_scalef32_pk_fp4_f32
+// with a unit scale performs exactly this rounding for every finite fp32 input.
+__device__ __forceinline__ uint32_t e2m1_rne_pack8(const float* z) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[0], z[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[2], z[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[4], z[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[6], z[7], 1.0f, 3);
+    return w;
 }
 
 // ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) --------------------------------------
@@ -114,8 +118,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
         if (i) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-        uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-        uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+        const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
         uint32_t n0 = hi1 ^ c1 ^ k0;
         uint32_t n2 = hi0 ^ c3 ^ k1;
         c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;

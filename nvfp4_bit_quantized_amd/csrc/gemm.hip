@@ -12,12 +12,16 @@
 // to v_mfma_f32_32x32x16_f16, which accumulates in fp32.  The per-tensor decode scales are
 // applied once in the epilogue.
 //
-// Data flow per workgroup (BM x BN output tile, K in steps of 64):
-//   global -> VGPR prefetch of packed codes (32 B per row per step) and scale bytes
-//   -> LDS (double buffered, half-swapped rows to spread LDS banks)
-//   -> each wave reads 16 B (32 codes) per 32-row MFMA tile and lane, unpacks 8 codes at a time
-//      with v_cvt_scalef32_pk_f16_fp4 and multiplies by its block scale (packed fp16)
-//   -> MFMA 32x32x16.
+// Workgroup: 8 waves (2 per SIMD), a 256 x 256 output tile, K in steps of 64.
+//   global -> VGPR prefetch two steps ahead (one 16-byte code chunk of A and of B and one
+//   dword of four scale bytes per thread and step)
+//   -> LDS, double buffered: codes [256][32 B] per operand with the two 16-byte halves swapped
+//      on rows with bit 2 set (spreads eight consecutive rows over all banks), scales as fp16
+//      pairs converted with v_cvt_scalef32_pk_f16_fp8
+//   -> each wave reads 16 B (32 codes) per 32-row MFMA tile and lane, unpacks 8 codes at a
+//      time with v_cvt_scalef32_pk_f16_fp4 and multiplies them by their block scale (v_pk_mul_f16)
+//   -> v_mfma_f32_32x32x16_f16.
+// The barrier between steps orders LDS only, so global prefetches stay in flight across it.
 // K is permuted inside a step identically for both operands: MFMA k-slot (8h + j) of sub-step
 // s reads element 32h + 8s + j of the 64-element step, so a lane's 16 bytes cover two whole
 // NVFP4 blocks and one scale serves each sub-step.
@@ -33,8 +37,10 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;            // K elements per pipeline step
-constexpr int kRowBytes = kBK / 2; // packed bytes per row per step
+constexpr int kBK = 64;             // K elements per pipeline step
+constexpr int kRowBytes = kBK / 2;  // packed bytes per row per step
+constexpr int kTile = 256;          // BM = BN
+constexpr int kThreads = 512;       // 8 waves
 
 // 8 E2M1 codes (one dword, element 2j in the low nibble of byte j) times a scale -> 8 fp16.
 __device__ __forceinline__ half8 unpack8(uint32_t w, half2v s2) {
@@ -46,6 +52,13 @@ __device__ __forceinline__ half8 unpack8(uint32_t w, half2v s2) {
     r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
     r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
     return r;
+}
+
+// Workgroup barrier that orders LDS accesses only: outstanding global loads are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 struct OperandDesc {
@@ -72,147 +85,342 @@ __device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t nbm, uint32_t
     bn = in / gm;
 }
 
-template <int WM, int WN, int TM, int TN>
-struct GemmCfg {
-    static constexpr int kWaves = WM * WN;
-    static constexpr int kThreads = kWaves * 64;
-    static constexpr int BM = WM * TM * 32;
-    static constexpr int BN = WN * TN * 32;
+// One K step of one workgroup in LDS.
+struct alignas(16) LdsStep {
+    uint8_t a[kTile * kRowBytes];
+    uint8_t b[kTile * kRowBytes];
+    uint2 sa[kTile];        // fp16 scale pairs: {s0,s1}, {s2,s3} per row
+    uint2 sb[kTile];
 };
 
-// E4M3 scale byte -> fp16 bits, duplicated into both halves of a dword (exact conversion).
-__device__ __forceinline__ uint32_t scale_splat(uint32_t b) {
-    const _Float16 h = (_Float16)e4m3_decode(b);
-    const uint32_t u = (uint32_t)__builtin_bit_cast(uint16_t, h);
-    return u | (u << 16);
-}
-
-// LDS image of one operand tile for one K step:
-//   codes  [ROWS][32 B]: the two 16-byte halves of a row swapped on rows with bit 2 set, which
-//          spreads the 16-byte lane reads of eight consecutive rows over all banks;
-//   scales [ROWS][4 dwords]: the four block scales of the step as fp16 pairs (s, s).
-template <int ROWS>
-struct LdsTile {
-    uint8_t codes[ROWS * kRowBytes];
-    uint4 scales[ROWS];
-};
-
-template <int ROWS, int NT>
-__device__ __forceinline__ void store_stage(LdsTile<ROWS>& t, const uint4* c, uint32_t s, int tid) {
-    constexpr int kPer = (ROWS * 2 + NT - 1) / NT;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int ch = tid + i * NT;
-        if (ch < ROWS * 2) {
-            const int r = ch >> 1, h = (ch & 1) ^ ((r >> 2) & 1);
-            *reinterpret_cast<uint4*>(t.codes + r * kRowBytes + h * 16) = c[i];
-        }
-    }
-    if (tid < ROWS)
-        t.scales[tid] = make_uint4(scale_splat(s & 0xFFu), scale_splat((s >> 8) & 0xFFu),
-                                   scale_splat((s >> 16) & 0xFFu), scale_splat(s >> 24));
-}
-
-// Global loads of one operand for K % 64 == 0: every thread keeps its own row pointers (rows
-// past the end are clamped to the last row; their results are never stored) and advances them
-// by one step (32 code bytes, 4 scale bytes) per load, so the loop has no branches and no
-// 64-bit multiplies.
-template <int ROWS, int NT>
-struct FastLoader {
-    static constexpr int kPer = (ROWS * 2 + NT - 1) / NT;
-    const uint8_t* pc[kPer];
-    const uint8_t* ps;
-    uint4 c[kPer];
+// What one thread fetches for one K step: A code chunk (thread t: row t/2, half t%2), B code
+// chunk (same), and the four scale bytes of row t (t < 256: A) or row t-256 (B).
+struct Fetch {
+    uint4 a, b;
     uint32_t s;
+};
 
-    __device__ __forceinline__ void init(const OperandDesc& op, int64_t row0, int K, int tid) {
-        const int64_t last = op.rows - 1;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int ch = (tid + i * NT) % (ROWS * 2);
-            int64_t row = row0 + (ch >> 1);
-            row = row < last ? row : last;
-            pc[i] = op.codes + row * (K / 2) + (ch & 1) * 16;
-        }
-        int64_t srow = row0 + (tid % ROWS);
-        srow = srow < last ? srow : last;
-        ps = op.scales + (op.tiled ? srow / 16 : srow) * (K / 16);
+// Global addressing for K % 64 == 0: per-thread pointers (rows past the end clamped to the last
+// row, whose results are never stored), advanced by one step per fetch.
+struct FastAddr {
+    const uint8_t *pa, *pb, *ps;
+    __device__ __forceinline__ void init(const OperandDesc& A, const OperandDesc& B, int64_t m0,
+                                         int64_t n0, int K, int t) {
+        const int r = t >> 1, h = t & 1;
+        int64_t ra = m0 + r, rb = n0 + r;
+        ra = ra < A.rows - 1 ? ra : A.rows - 1;
+        rb = rb < B.rows - 1 ? rb : B.rows - 1;
+        pa = A.codes + ra * (K / 2) + h * 16;
+        pb = B.codes + rb * (K / 2) + h * 16;
+        const OperandDesc& S = t < kTile ? A : B;
+        int64_t rs = (t < kTile ? m0 : n0) + (t & (kTile - 1));
+        rs = rs < S.rows - 1 ? rs : S.rows - 1;
+        ps = S.scales + (S.tiled ? rs / 16 : rs) * (K / 16);
     }
-    __device__ __forceinline__ void load() {
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            c[i] = *reinterpret_cast<const uint4*>(pc[i]);
-            pc[i] += kRowBytes;
-        }
-        s = *reinterpret_cast<const uint32_t*>(ps);
+    __device__ __forceinline__ Fetch fetch(int) {
+        Fetch f;
+        f.a = *reinterpret_cast<const uint4*>(pa);
+        f.b = *reinterpret_cast<const uint4*>(pb);
+        f.s = *reinterpret_cast<const uint32_t*>(ps);
+        pa += kRowBytes;
+        pb += kRowBytes;
         ps += 4;
+        return f;
     }
 };
 
-// Guarded loads for any K % 16 == 0 (zero codes past K and past the last row).
-template <int ROWS, int NT>
-struct GuardedLoader {
-    static constexpr int kPer = (ROWS * 2 + NT - 1) / NT;
-    OperandDesc op;
-    int64_t row0;
-    int K, k0;
-    uint4 c[kPer];
-    uint32_t s;
-
-    __device__ __forceinline__ void init(const OperandDesc& o, int64_t r0, int k, int) {
-        op = o; row0 = r0; K = k; k0 = 0;
+// Guarded addressing for any K % 16 == 0: zero codes past K and past the last row.
+struct GuardedAddr {
+    OperandDesc A, B;
+    int64_t m0, n0;
+    int K, t;
+    __device__ __forceinline__ void init(const OperandDesc& a, const OperandDesc& b, int64_t m,
+                                         int64_t n, int k, int tid) {
+        A = a; B = b; m0 = m; n0 = n; K = k; t = tid;
     }
-    __device__ __forceinline__ void load_at(int tid) {
-        const int64_t rb = K / 2;
+    __device__ __forceinline__ uint4 chunk(const OperandDesc& op, int64_t row, int k0) const {
+        const int kk = k0 + (t & 1) * 32;
+        if (row >= op.rows || kk >= K) return make_uint4(0, 0, 0, 0);
+        const uint8_t* p = op.codes + row * (K / 2) + kk / 2;
+        if (kk + 32 <= K) return *reinterpret_cast<const uint4*>(p);
+        const uint2 v = *reinterpret_cast<const uint2*>(p);          // K % 32 == 16 tail
+        return make_uint4(v.x, v.y, 0, 0);
+    }
+    __device__ __forceinline__ Fetch fetch(int kt) {
+        Fetch f;
+        const int k0 = kt * kBK;
+        f.a = chunk(A, m0 + (t >> 1), k0);
+        f.b = chunk(B, n0 + (t >> 1), k0);
+        const OperandDesc& S = t < kTile ? A : B;
+        const int64_t row = (t < kTile ? m0 : n0) + (t & (kTile - 1));
+        f.s = 0;
+        if (row < S.rows) {
+            const int64_t nkb = K / 16;
+            const uint8_t* sp = S.scales + (S.tiled ? row / 16 : row) * nkb;
+            const int kb0 = k0 / 16;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int ch = tid + i * NT;
-            c[i] = make_uint4(0, 0, 0, 0);
-            if (ch < ROWS * 2) {
-                const int64_t row = row0 + (ch >> 1);
-                const int kk = k0 + (ch & 1) * 32;
-                if (row < op.rows && kk < K) {
-                    const uint8_t* p = op.codes + row * rb + kk / 2;
-                    if (kk + 32 <= K) {
-                        c[i] = *reinterpret_cast<const uint4*>(p);
-                    } else {                                       // K % 32 == 16 tail
-                        const uint2 v = *reinterpret_cast<const uint2*>(p);
-                        c[i] = make_uint4(v.x, v.y, 0, 0);
-                    }
-                }
-            }
+            for (int b = 0; b < 4; ++b)
+                if (kb0 + b < nkb) f.s |= (uint32_t)sp[kb0 + b] << (8 * b);
         }
-        s = 0;
-        if (tid < ROWS) {
-            const int64_t row = row0 + tid;
-            if (row < op.rows) {
-                const int64_t nkb = K / 16;
-                const uint8_t* sp = op.tiled ? op.scales + (row / 16) * nkb : op.scales + row * nkb;
-                const int kb0 = k0 / 16;
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    if (kb0 + b < nkb) s |= (uint32_t)sp[kb0 + b] << (8 * b);
-            }
-        }
-        k0 += kBK;
+        return f;
     }
 };
 
-template <int WM, int WN, int TM, int TN, bool kBF16Out, bool kFast>
-__global__ void __launch_bounds__(WM * WN * 64)
+// Physical 16-byte half of logical half h of row r: swapped when bits 2 and 3 of r differ, so
+// that any 8 or 16 consecutive rows read at the same logical half hit distinct bank groups.
+__device__ __forceinline__ int half_swz(int r, int h) { return (h ^ (r >> 2) ^ (r >> 3)) & 1; }
+
+__device__ __forceinline__ void store_step(LdsStep& st, Fetch f, int t) {
+    const int r = t >> 1, h = half_swz(r, t & 1);
+    *reinterpret_cast<uint4*>(&st.a[r * kRowBytes + h * 16]) = f.a;
+    *reinterpret_cast<uint4*>(&st.b[r * kRowBytes + h * 16]) = f.b;
+    const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
+    const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, true);
+    const uint2 v = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    if (t < kTile) st.sa[t] = v; else st.sb[t - kTile] = v;
+}
+
+template <int WN, int TM, int TN>
+__device__ __forceinline__ void compute_step(const LdsStep& st, float16v (&acc)[TM][TN], int wm,
+                                             int wn, int lane) {
+    const int lrow = lane & 31, h = lane >> 5;
+    uint4 fa[TM], fb[TN];
+    half2v xa[TM], xb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * TM * 32 + i * 32 + lrow;
+        fa[i] = *reinterpret_cast<const uint4*>(&st.a[r * kRowBytes + half_swz(r, h) * 16]);
+        xa[i] = __builtin_bit_cast(half2v, reinterpret_cast<const uint32_t*>(&st.sa[r])[h]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * 32 + j * 32 + lrow;
+        fb[j] = *reinterpret_cast<const uint4*>(&st.b[r * kRowBytes + half_swz(r, h) * 16]);
+        xb[j] = __builtin_bit_cast(half2v, reinterpret_cast<const uint32_t*>(&st.sb[r])[h]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        // unpack this sub-step's A fragments, then each B fragment right before its MFMAs, so
+        // few unpacked operands are live at once
+        half8 va[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const uint32_t w = s == 0 ? fa[i].x : s == 1 ? fa[i].y : s == 2 ? fa[i].z : fa[i].w;
+            const _Float16 sc = xa[i][s >> 1];
+            va[i] = unpack8(w, half2v{sc, sc});
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const uint32_t w = s == 0 ? fb[j].x : s == 1 ? fb[j].y : s == 2 ? fb[j].z : fb[j].w;
+            const _Float16 sc = xb[j][s >> 1];
+            const half8 vb = unpack8(w, half2v{sc, sc});
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb, acc[i][j], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// ---- unpack-once variant -------------------------------------------------------------------
+// The loading threads turn their code chunk into scaled fp16 right away and store it to LDS,
+// so every element is unpacked once per workgroup instead of once per wave that reads it;
+// waves then read MFMA-ready fp16 fragments.  LDS per step: [256][64] fp16 per operand, with
+// the eight 16-byte chunks of a row permuted by chunk ^ (r & 7) ^ ((r >> 3) & 1) so that 8 or
+// 16 consecutive rows reading the same logical chunk hit distinct bank groups.
+struct alignas(16) LdsStepU {
+    _Float16 a[kTile * kBK];
+    _Float16 b[kTile * kBK];
+};
+
+struct FetchU {
+    uint4 a, b;
+    uint32_t s;     // A's two scale bytes (low half) and B's (high half) for this chunk
+};
+
+__device__ __forceinline__ int chunk_swz(int r, int q) { return q ^ (r & 7) ^ ((r >> 3) & 1); }
+
+struct FastAddrU {
+    const uint8_t *pa, *pb, *psa, *psb;
+    __device__ __forceinline__ void init(const OperandDesc& A, const OperandDesc& B, int64_t m0,
+                                         int64_t n0, int K, int t) {
+        const int r = t >> 1, h = t & 1;
+        int64_t ra = m0 + r, rb = n0 + r;
+        ra = ra < A.rows - 1 ? ra : A.rows - 1;
+        rb = rb < B.rows - 1 ? rb : B.rows - 1;
+        pa = A.codes + ra * (K / 2) + h * 16;
+        pb = B.codes + rb * (K / 2) + h * 16;
+        psa = A.scales + (A.tiled ? ra / 16 : ra) * (K / 16) + h * 2;
+        psb = B.scales + (B.tiled ? rb / 16 : rb) * (K / 16) + h * 2;
+    }
+    __device__ __forceinline__ FetchU fetch(int) {
+        FetchU f;
+        f.a = *reinterpret_cast<const uint4*>(pa);
+        f.b = *reinterpret_cast<const uint4*>(pb);
+        f.s = (uint32_t)*reinterpret_cast<const uint16_t*>(psa) |
+              ((uint32_t)*reinterpret_cast<const uint16_t*>(psb) << 16);
+        pa += kRowBytes;
+        pb += kRowBytes;
+        psa += 4;
+        psb += 4;
+        return f;
+    }
+};
+
+struct GuardedAddrU {
+    OperandDesc A, B;
+    int64_t m0, n0;
+    int K, t;
+    __device__ __forceinline__ void init(const OperandDesc& a, const OperandDesc& b, int64_t m,
+                                         int64_t n, int k, int tid) {
+        A = a; B = b; m0 = m; n0 = n; K = k; t = tid;
+    }
+    __device__ __forceinline__ uint4 chunk(const OperandDesc& op, int64_t row, int k0) const {
+        const int kk = k0 + (t & 1) * 32;
+        if (row >= op.rows || kk >= K) return make_uint4(0, 0, 0, 0);
+        const uint8_t* p = op.codes + row * (K / 2) + kk / 2;
+        if (kk + 32 <= K) return *reinterpret_cast<const uint4*>(p);
+        const uint2 v = *reinterpret_cast<const uint2*>(p);          // K % 32 == 16 tail
+        return make_uint4(v.x, v.y, 0, 0);
+    }
+    __device__ __forceinline__ uint32_t scales2(const OperandDesc& op, int64_t row, int k0) const {
+        if (row >= op.rows) return 0;
+        const int64_t nkb = K / 16;
+        const uint8_t* sp = op.scales + (op.tiled ? row / 16 : row) * nkb;
+        const int kb = k0 / 16 + (t & 1) * 2;
+        uint32_t v = 0;
+        if (kb < nkb) v |= sp[kb];
+        if (kb + 1 < nkb) v |= (uint32_t)sp[kb + 1] << 8;
+        return v;
+    }
+    __device__ __forceinline__ FetchU fetch(int kt) {
+        FetchU f;
+        const int k0 = kt * kBK;
+        const int64_t ra = m0 + (t >> 1), rb = n0 + (t >> 1);
+        f.a = chunk(A, ra, k0);
+        f.b = chunk(B, rb, k0);
+        f.s = scales2(A, ra, k0) | (scales2(B, rb, k0) << 16);
+        return f;
+    }
+};
+
+__device__ __forceinline__ void store_one_u(_Float16* rowp, int r, int h, uint4 c, half2v sc) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const _Float16 s = sc[d >> 1];
+        const half8 v = unpack8(w[d], half2v{s, s});
+        *reinterpret_cast<half8*>(rowp + 8 * chunk_swz(r, 4 * h + d)) = v;
+    }
+}
+
+__device__ __forceinline__ void store_step_u(LdsStepU& st, FetchU f, int t) {
+    const int r = t >> 1, h = t & 1;
+    const half2v sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
+    const half2v sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, true);
+    store_one_u(&st.a[r * kBK], r, h, f.a, sa);
+    store_one_u(&st.b[r * kBK], r, h, f.b, sb);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void read_frags_u(const LdsStepU& st, half8 (&va)[TM], half8 (&vb)[TN],
+                                             int wm, int wn, int lane, int s) {
+    const int lrow = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * TM * 32 + i * 32 + lrow;
+        va[i] = *reinterpret_cast<const half8*>(&st.a[r * kBK + 8 * chunk_swz(r, 4 * h + s)]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * 32 + j * 32 + lrow;
+        vb[j] = *reinterpret_cast<const half8*>(&st.b[r * kBK + 8 * chunk_swz(r, 4 * h + s)]);
+    }
+}
+
+// One K step: MFMAs on `cur` and, interleaved with them, the unpack/store of the next step's
+// fetched codes into `nxt` (a quarter after each sub-step's MFMAs), so that the VALU and LDS
+// work overlaps the matrix-core work instead of running between barriers.  Fragments for
+// sub-step s + 1 are read while sub-step s computes.
+template <int TM, int TN>
+__device__ __forceinline__ void step_u(const LdsStepU& cur, LdsStepU& nxt, const FetchU& f,
+                                       bool do_store, float16v (&acc)[TM][TN], int wm, int wn,
+                                       int lane, int tid) {
+    const int r = tid >> 1, h = tid & 1;
+    const half2v sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, false);
+    const half2v sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.s, 1.0f, true);
+    const uint32_t wa[4] = {f.a.x, f.a.y, f.a.z, f.a.w}, wb[4] = {f.b.x, f.b.y, f.b.z, f.b.w};
+    half8 va[2][TM], vb[2][TN];
+    read_frags_u<TM, TN>(cur, va[0], vb[0], wm, wn, lane, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int c = s & 1;
+        if (s < 3) read_frags_u<TM, TN>(cur, va[c ^ 1], vb[c ^ 1], wm, wn, lane, s + 1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[c][i], vb[c][j], acc[i][j], 0, 0, 0);
+        if (do_store) {
+            const _Float16 xa = sa[s >> 1], xb = sb[s >> 1];
+            const int p = 8 * chunk_swz(r, 4 * h + s);
+            *reinterpret_cast<half8*>(&nxt.a[r * kBK + p]) = unpack8(wa[s], half2v{xa, xa});
+            *reinterpret_cast<half8*>(&nxt.b[r * kBK + p]) = unpack8(wb[s], half2v{xb, xb});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Pipelines shared by both variants: register prefetch two steps ahead, LDS double buffer.
+struct PackedMode {
+    using Step = LdsStep;
+    template <int WN, int TM, int TN>
+    static __device__ __forceinline__ void compute(const Step& st, float16v (&acc)[TM][TN], int wm,
+                                                   int wn, int lane) {
+        compute_step<WN, TM, TN>(st, acc, wm, wn, lane);
+    }
+    template <typename F>
+    static __device__ __forceinline__ void store(Step& st, F f, int t) { store_step(st, f, t); }
+    template <int WN, int TM, int TN, typename F>
+    static __device__ __forceinline__ void compute_store(const Step& cur, Step& nxt, const F& f,
+                                                         bool do_store, float16v (&acc)[TM][TN],
+                                                         int wm, int wn, int lane, int tid) {
+        compute_step<WN, TM, TN>(cur, acc, wm, wn, lane);
+        if (do_store) store_step(nxt, f, tid);
+    }
+};
+
+struct UnpackedMode {
+    using Step = LdsStepU;
+    template <int WN, int TM, int TN>
+    static __device__ __forceinline__ void compute(const Step& st, float16v (&acc)[TM][TN], int wm,
+                                                   int wn, int lane) {
+        FetchU none{};
+        step_u<TM, TN>(st, const_cast<Step&>(st), none, false, acc, wm, wn, lane, 0);
+    }
+    template <typename F>
+    static __device__ __forceinline__ void store(Step& st, F f, int t) { store_step_u(st, f, t); }
+    template <int WN, int TM, int TN, typename F>
+    static __device__ __forceinline__ void compute_store(const Step& cur, Step& nxt, const F& f,
+                                                         bool do_store, float16v (&acc)[TM][TN],
+                                                         int wm, int wn, int lane, int tid) {
+        step_u<TM, TN>(cur, nxt, f, do_store, acc, wm, wn, lane, tid);
+    }
+};
+
+// Waves are arranged WM x WN over the 256 x 256 tile, each owning TM x TN MFMA tiles of 32x32.
+template <int WM, int WN, int TM, int TN, bool kBF16Out, typename Mode, typename Addr>
+__global__ void __launch_bounds__(kThreads)
 k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __restrict__ sdA,
              const float* __restrict__ sdB, void* __restrict__ C, int64_t ldc) {
-    using Cfg = GemmCfg<WM, WN, TM, TN>;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::kThreads;
-    __shared__ __attribute__((aligned(16))) LdsTile<BM> lds_a[2];
-    __shared__ __attribute__((aligned(16))) LdsTile<BN> lds_b[2];
-
+    static_assert(WM * WN == kThreads / 64 && WM * TM * 32 == kTile && WN * TN * 32 == kTile, "tile");
+    __shared__ typename Mode::Step st[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const uint32_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+    const uint32_t nbm = (M + kTile - 1) / kTile, nbn = (N + kTile - 1) / kTile;
     uint32_t bm, bn;
     tile_coords(blockIdx.x, nbm, nbn, bm, bn);
-    const int64_t m0 = (int64_t)bm * BM, n0 = (int64_t)bn * BN;
+    const int64_t m0 = (int64_t)bm * kTile, n0 = (int64_t)bn * kTile;
 
     float16v acc[TM][TN];
 #pragma unroll
@@ -222,71 +430,30 @@ k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __r
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    using LA = typename std::conditional<kFast, FastLoader<BM, NT>, GuardedLoader<BM, NT>>::type;
-    using LB = typename std::conditional<kFast, FastLoader<BN, NT>, GuardedLoader<BN, NT>>::type;
-    LA la;
-    LB lb;
-    la.init(A, m0, K, tid);
-    lb.init(B, n0, K, tid);
-    auto load = [&]() {
-        if constexpr (kFast) { la.load(); lb.load(); }
-        else { la.load_at(tid); lb.load_at(tid); }
-    };
+    Addr addr;
+    addr.init(A, B, m0, n0, K, tid);
     const int nk = (K + kBK - 1) / kBK;
-    load();
-    store_stage<BM, NT>(lds_a[0], la.c, la.s, tid);
-    store_stage<BN, NT>(lds_b[0], lb.c, lb.s, tid);
-    __syncthreads();
-
-    const int lrow = lane & 31, h = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load();
-        // fragments: 16 bytes (32 codes) and 2 scale pairs per tile and lane
-        uint4 fa[TM], fb[TN];
-        uint2 xa[TM], xb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = wm * TM * 32 + i * 32 + lrow;
-            const int hh = h ^ ((r >> 2) & 1);
-            fa[i] = *reinterpret_cast<const uint4*>(&lds_a[cur].codes[r * kRowBytes + hh * 16]);
-            xa[i] = reinterpret_cast<const uint2*>(&lds_a[cur].scales[r])[h];
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int r = wn * TN * 32 + j * 32 + lrow;
-            const int hh = h ^ ((r >> 2) & 1);
-            fb[j] = *reinterpret_cast<const uint4*>(&lds_b[cur].codes[r * kRowBytes + hh * 16]);
-            xb[j] = reinterpret_cast<const uint2*>(&lds_b[cur].scales[r])[h];
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            half8 va[TM], vb[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const uint32_t w = s == 0 ? fa[i].x : s == 1 ? fa[i].y : s == 2 ? fa[i].z : fa[i].w;
-                va[i] = unpack8(w, __builtin_bit_cast(half2v, s < 2 ? xa[i].x : xa[i].y));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const uint32_t w = s == 0 ? fb[j].x : s == 1 ? fb[j].y : s == 2 ? fb[j].z : fb[j].w;
-                vb[j] = unpack8(w, __builtin_bit_cast(half2v, s < 2 ? xb[j].x : xb[j].y));
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[i], vb[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-            store_stage<BM, NT>(lds_a[cur ^ 1], la.c, la.s, tid);
-            store_stage<BN, NT>(lds_b[cur ^ 1], lb.c, lb.s, tid);
-        }
-        __syncthreads();
+    auto f0 = addr.fetch(0), f1 = f0;
+    Mode::store(st[0], f0, tid);
+    if (nk > 1) f1 = addr.fetch(1);
+    lds_barrier();
+    // Two steps per trip so that the register sets and LDS buffers have fixed roles:
+    // step kt computes st[kt % 2], fetches step kt + 2 and stores step kt + 1.  An odd last
+    // step is peeled off after the loop.
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        if (kt + 2 < nk) f0 = addr.fetch(kt + 2);
+        Mode::template compute_store<WN, TM, TN>(st[0], st[1], f1, true, acc, wm, wn, lane, tid);
+        lds_barrier();
+        if (kt + 3 < nk) f1 = addr.fetch(kt + 3);
+        Mode::template compute_store<WN, TM, TN>(st[1], st[0], f0, kt + 2 < nk, acc, wm, wn, lane, tid);
+        lds_barrier();
     }
+    if (kt < nk) Mode::template compute<WN, TM, TN>(st[0], acc, wm, wn, lane);
 
     // epilogue: D element r of lane l sits at row 8*(r/4) + 4*(l/32) + r%4, column l%32
     const float alpha = (*sdA) * (*sdB);
+    const int lrow = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -307,21 +474,23 @@ k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __r
         }
 }
 
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, bool kUnpackOnce>
 static void launch_gemm(const OperandDesc& a, const OperandDesc& b, int M, int N, int K,
                         const float* sdA, const float* sdB, void* c, bool bf16, int64_t ldc,
                         hipStream_t st) {
-    using Cfg = GemmCfg<WM, WN, TM, TN>;
-    const uint32_t nbm = (M + Cfg::BM - 1) / Cfg::BM, nbn = (N + Cfg::BN - 1) / Cfg::BN;
-    const dim3 grid(nbm * nbn), block(Cfg::kThreads);
+    const uint32_t nbm = (M + kTile - 1) / kTile, nbn = (N + kTile - 1) / kTile;
+    const dim3 grid(nbm * nbn), block(kThreads);
     const bool fast = K % kBK == 0;
-#define NVFP4_GEMM_LAUNCH(BF, FAST)                                                               \
-    hipLaunchKernelGGL((k_gemm_nvfp4<WM, WN, TM, TN, BF, FAST>), grid, block, 0, st, a, b, M, N, K, \
-                       sdA, sdB, c, ldc)
+    using Mode = typename std::conditional<kUnpackOnce, UnpackedMode, PackedMode>::type;
+    using AF = typename std::conditional<kUnpackOnce, FastAddrU, FastAddr>::type;
+    using AG = typename std::conditional<kUnpackOnce, GuardedAddrU, GuardedAddr>::type;
+#define NVFP4_GEMM_LAUNCH(BF, ADDR)                                                               \
+    hipLaunchKernelGGL((k_gemm_nvfp4<WM, WN, TM, TN, BF, Mode, ADDR>), grid, block, 0, st, a, b, M, \
+                       N, K, sdA, sdB, c, ldc)
     if (bf16) {
-        if (fast) NVFP4_GEMM_LAUNCH(true, true); else NVFP4_GEMM_LAUNCH(true, false);
+        if (fast) NVFP4_GEMM_LAUNCH(true, AF); else NVFP4_GEMM_LAUNCH(true, AG);
     } else {
-        if (fast) NVFP4_GEMM_LAUNCH(false, true); else NVFP4_GEMM_LAUNCH(false, false);
+        if (fast) NVFP4_GEMM_LAUNCH(false, AF); else NVFP4_GEMM_LAUNCH(false, AG);
     }
 #undef NVFP4_GEMM_LAUNCH
 }
@@ -347,7 +516,7 @@ extern "C" nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     if (M == 0 || N == 0) return NVFP4_OK;
     const OperandDesc da{a->codes, a->scales, M, 0};
     const OperandDesc db{b->codes, b->scales, N, b->layout == NVFP4_BLK_16x16 ? 1 : 0};
-    launch_gemm<2, 2, 4, 4>(da, db, (int)M, (int)N, (int)K, a->s_dec, b->s_dec, c,
+    launch_gemm<2, 4, 4, 2, true>(da, db, (int)M, (int)N, (int)K, a->s_dec, b->s_dec, c,
                             c_dt == NVFP4_BF16, ldc, as_stream(stream));
     return launch_status();
 }

@@ -165,21 +165,20 @@ k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t
             const uint64_t idx = (uint64_t)feat * (uint64_t)Tn + (uint64_t)rc.c * 16;
             const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
             const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+            float z[16];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t ra = (e & 1) ? (a[e >> 1] >> 16) : (a[e >> 1] & 0xFFFFu);
-                const uint32_t rb = (e & 1) ? (b[e >> 1] >> 16) : (b[e >> 1] & 0xFFFFu);
-                const float za = v[e] * enc, zb = v[e + 8] * enc;
-                lo |= e2m1_sr_code2(za + za, ra) << (4 * e);
-                hi |= e2m1_sr_code2(zb + zb, rb) << (4 * e);
+            for (int e = 0; e < 16; ++e) {
+                const float ze = v[e] * enc;
+                z[e] = ze + ze;
             }
+            lo = e2m1_sr_pack8(z, a);
+            hi = e2m1_sr_pack8(z + 8, b);
         } else {
-            const float enc2 = enc + enc;
+            float z[16];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                lo |= e2m1_rne_code2(v[e] * enc2) << (4 * e);
-                hi |= e2m1_rne_code2(v[e + 8] * enc2) << (4 * e);
-            }
+            for (int e = 0; e < 16; ++e) z[e] = v[e] * enc;
+            lo = e2m1_rne_pack8(z);
+            hi = e2m1_rne_pack8(z + 8);
         }
         if (feat < F) {
             *reinterpret_cast<uint2*>(codes + feat * (Tn / 2) + rc.c * 8) = make_uint2(lo, hi);

@@ -5,11 +5,10 @@
 // [P2] "FP4 All the Way: Formacion totalmente cuantificada de LLM"; [P3] "I ricercatori di
 // Nvidia sbloccano il tutorial LLM a 8 bit che corrisponde alle prestazioni a 4 bit".
 //
-// All kernels here are HBM-bound streaming kernels.  Work is split into "groups" of 8
-// consecutive elements of a row: one 16-byte load for bf16 (two for fp32), one 32-bit store of
-// 8 packed codes.  Two adjacent lanes hold one 16-element NVFP4 block and exchange their partial
-// amax with a single DPP lane swap.  Each thread handles UNROLL groups whose loads are issued
-// before any arithmetic, to keep enough bytes in flight.
+// All kernels here are HBM-bound streaming kernels.  The amax, dequantize and MXFP4 kernels
+// split rows into "groups" of 8 consecutive elements (one 16-byte bf16 load, one 32-bit store of
+// 8 packed codes); the NVFP4 1D quantizer gives each lane a whole 16-element block.  Every
+// thread issues all of its loads before any arithmetic, to keep enough bytes in flight.
 
 #include "device_codecs.hpp"
 #include "host_util.hpp"
@@ -17,7 +16,8 @@
 namespace nvfp4 {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;     // groups per thread and trip in the amax / dequantize / MX kernels
+constexpr int kQUnroll = 8;    // groups per thread in the NVFP4 1D quantizer
 
 // 8 input elements of one group as fp32.
 template <typename T> struct Group8;
@@ -102,10 +102,13 @@ static int amax_grid(uint32_t groups) {
 }
 
 // ---- 1D quantization [P1 Caracteristicas; P2 Describir] ---------------------------------------
+// One lane owns one whole 16-element block: two 16-byte loads (bf16), one 8-byte code store and
+// one scale byte.  Each thread handles kQUnroll blocks spaced a workgroup apart, all loads first.
+// Blocks past the end load a clamped (valid) block and store nothing.
 template <typename T, bool kSR>
 __global__ void __launch_bounds__(kThreads)
-k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, uint32_t cols,
-          const float* __restrict__ amax_src, uint64_t seed, uint32_t* __restrict__ codes,
+k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uint32_t cols,
+          const float* __restrict__ amax_src, uint64_t seed, uint2* __restrict__ codes,
           uint8_t* __restrict__ scales, float* amax_out, float* sdec_out) {
     const float A = *amax_src;
     const TensorScales ts = tensor_scales(A);
@@ -113,51 +116,51 @@ k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, uin
         *amax_out = A;
         *sdec_out = ts.s_dec;
     }
-    const uint32_t base = blockIdx.x * kThreads * kUnroll + threadIdx.x;
-    float y[kUnroll][8];
-    uint32_t row[kUnroll], cg[kUnroll];
+    const uint32_t base = blockIdx.x * kThreads * kQUnroll + threadIdx.x;
+    float y[kQUnroll][16];
+    uint32_t row[kQUnroll], cb[kQUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        uint32_t g = base + u * kThreads;
-        row[u] = 0; cg[u] = 0;
-        if (g < groups) {
-            row[u] = fastdiv(g, gpr);
-            cg[u] = g - row[u] * gpr.d;
-            Group8<T>::load(x + (int64_t)row[u] * ld + cg[u] * 8, y[u]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[u][e] = 0.0f;
-        }
+    for (int u = 0; u < kQUnroll; ++u) {
+        uint32_t b = base + u * kThreads;
+        b = b < blocks ? b : blocks - 1;
+        row[u] = fastdiv(b, bpr);
+        cb[u] = b - row[u] * bpr.d;
+        const T* p = x + (int64_t)row[u] * ld + cb[u] * 16;
+        Group8<T>::load(p, y[u]);
+        Group8<T>::load(p + 8, y[u] + 8);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t g = base + u * kThreads;
+    for (int u = 0; u < kQUnroll; ++u) {
+        const uint32_t b = base + u * kThreads;
         float m = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[u][e]));
-        m = fmaxf(m, swap_adjacent(m));          // amax of the 16-element block
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(y[u][e]));
         uint32_t sb;
         float enc;
         block_scale(m, ts, sb, enc);
-        uint32_t packed = 0;
+        uint32_t lo = 0, hi = 0;
         if constexpr (kSR) {
-            const uint64_t idx8 = (uint64_t)row[u] * cols + cg[u] * 8;
-            const u32x4 w = sr_words(seed, idx8);
-            const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+            const uint64_t idx = (uint64_t)row[u] * cols + cb[u] * 16;
+            const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
+            const uint32_t wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
+            float z[16];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float z = y[u][e] * enc;
-                uint32_t r16 = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
-                packed |= e2m1_sr_code2(z + z, r16) << (4 * e);
+            for (int e = 0; e < 16; ++e) {
+                const float ze = y[u][e] * enc;
+                z[e] = ze + ze;
             }
+            lo = e2m1_sr_pack8(z, wa);
+            hi = e2m1_sr_pack8(z + 8, wb);
         } else {
-            const float enc2 = enc + enc;
+            float z[16];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) packed |= e2m1_rne_code2(y[u][e] * enc2) << (4 * e);
+            for (int e = 0; e < 16; ++e) z[e] = y[u][e] * enc;
+            lo = e2m1_rne_pack8(z);
+            hi = e2m1_rne_pack8(z + 8);
         }
-        if (g < groups) {
-            codes[g] = packed;                   // groups are dense in the code array
-            if ((g & 1u) == 0) scales[g >> 1] = (uint8_t)sb;
+        if (b < blocks) {
+            codes[b] = make_uint2(lo, hi);       // blocks are dense in the code array
+            scales[b] = (uint8_t)sb;
         }
     }
 }
@@ -206,20 +209,17 @@ k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols, uin
     uint32_t sb;
     float enc;
     block_scale(m, ts, sb, enc);
-    const float enc2 = enc + enc;
-    uint32_t c8[16];
+    float z[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) c8[e] = e2m1_rne_code2(y[e] * enc2);
-    uint32_t lo = 0, hi = 0;
+    for (int e = 0; e < 16; ++e) z[e] = y[e] * enc;
+    const uint32_t lo = e2m1_rne_pack8(z), hi = e2m1_rne_pack8(z + 8);
+    // one code per byte for the transposed copy
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        lo |= c8[e] << (4 * e);
-        hi |= c8[e + 8] << (4 * e);
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w = q < 2 ? lo : hi, sh = 16 * (q & 1);
+        const uint32_t n = (w >> sh) & 0xFFFFu;                 // codes 4q .. 4q+3
+        stage[wv][t][r][q] = (n & 0xFu) | ((n & 0xF0u) << 4) | ((n & 0xF00u) << 8) | ((n & 0xF000u) << 12);
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        stage[wv][t][r][q] = c8[4 * q] | (c8[4 * q + 1] << 8) | (c8[4 * q + 2] << 16) |
-                             (c8[4 * q + 3] << 24);
     if (valid) {
         *reinterpret_cast<uint2*>(codes + (int64_t)(ti * 16 + r) * (cols / 2) + tj * 8) =
             make_uint2(lo, hi);
@@ -329,16 +329,18 @@ k_mx_quant(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, ui
             const uint64_t idx8 = (uint64_t)row[u] * cols + cg[u] * 8;
             const u32x4 w = sr_words(seed, idx8);
             const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+            float z[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float z = __builtin_amdgcn_ldexpf(y[u][e], -e8);
-                uint32_t r16 = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
-                packed |= e2m1_sr_code2(z + z, r16) << (4 * e);
+                const float ze = __builtin_amdgcn_ldexpf(y[u][e], -e8);
+                z[e] = ze + ze;
             }
+            packed = e2m1_sr_pack8(z, words);
         } else {
+            float z[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                packed |= e2m1_rne_code2(__builtin_amdgcn_ldexpf(y[u][e], 1 - e8)) << (4 * e);
+            for (int e = 0; e < 8; ++e) z[e] = __builtin_amdgcn_ldexpf(y[u][e], -e8);
+            packed = e2m1_rne_pack8(z);
         }
         if (g < groups) {
             codes[g] = packed;
@@ -347,8 +349,8 @@ k_mx_quant(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, ui
     }
 }
 
-static int stream_grid(uint32_t groups) {
-    int64_t n = ((int64_t)groups + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+static int stream_grid(uint32_t groups, int unroll = kUnroll) {
+    int64_t n = ((int64_t)groups + kThreads * unroll - 1) / (kThreads * unroll);
     return (int)(n < 1 ? 1 : n);
 }
 
@@ -419,18 +421,18 @@ extern "C" nvfp4_status nvfp4_quantize_1d(const void* x, nvfp4_dtype dt, int64_t
         if (s) return s;
         src = out->amax;
     }
-    const uint32_t groups = (uint32_t)(out->rows * (out->cols / 8));
-    if (groups == 0) {
+    const uint32_t blocks = (uint32_t)(out->rows * (out->cols / 16));
+    if (blocks == 0) {
         hipLaunchKernelGGL(k_tensor_scalars, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
         return launch_status();
     }
-    const FastDiv gpr = make_fastdiv((uint32_t)(out->cols / 8));
-    const dim3 grid(stream_grid(groups)), block(kThreads);
-    uint32_t* codes = reinterpret_cast<uint32_t*>(out->codes);
+    const FastDiv bpr = make_fastdiv((uint32_t)(out->cols / 16));
+    const dim3 grid(stream_grid(blocks, kQUnroll)), block(kThreads);
+    uint2* codes = reinterpret_cast<uint2*>(out->codes);
     const uint32_t cols = (uint32_t)out->cols;
 #define NVFP4_Q1(T, SRV)                                                                         \
     hipLaunchKernelGGL((k_quant1d<T, SRV>), grid, block, 0, st, static_cast<const T*>(x), ld,     \
-                       groups, gpr, cols, src, seed, codes, out->scales, out->amax, out->s_dec)
+                       blocks, bpr, cols, src, seed, codes, out->scales, out->amax, out->s_dec)
     if (dt == NVFP4_BF16) {
         if (rnd == NVFP4_SR) NVFP4_Q1(uint16_t, true); else NVFP4_Q1(uint16_t, false);
     } else {
