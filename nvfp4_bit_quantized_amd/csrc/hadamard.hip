@@ -98,24 +98,33 @@ __device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
     return rc;
 }
 
+// Persistent over (64-feature x 512-token) tiles, at most kRhtAmaxBlocks workgroups, one
+// device-scope atomicMax per workgroup.
+constexpr int kRhtAmaxBlocks = 512;
+
 template <typename T>
 __global__ void __launch_bounds__(kRhtThreads)
 k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
-           float* amax_out) {
-    const RhtCoords rc = rht_coords(Tn, F);
+           float* amax_out, uint32_t tiles, FastDiv tiles_per_row) {
     const uint32_t mask = rht_sign_mask(sign_seed);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float m = 0.0f;
-    if (rc.valid) {
-        Tile16x8<T> tile;
-        tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+    for (uint32_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const uint32_t ty = fastdiv(tile, tiles_per_row), tx = tile - ty * tiles_per_row.d;
+        const int64_t f0 = (int64_t)tx * kFeatPerBlock + (lane & 7) * 8;
+        const int64_t c = (int64_t)ty * kChunksPerBlock + wave * 8 + (lane >> 3);
+        if (f0 < F && c * 16 < Tn) {
+            Tile16x8<T> t16;
+            t16.load(x + c * 16 * ld + f0, ld);
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            float v[16];
+            for (int f = 0; f < 8; ++f) {
+                float v[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
-            rht16(v, mask);
+                for (int i = 0; i < 16; ++i) v[i] = t16.get(i, f);
+                rht16(v, mask);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+                for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+            }
         }
     }
 #pragma unroll
@@ -204,12 +213,16 @@ static nvfp4_status launch_rht_amax(const void* x, nvfp4_dtype dt, int64_t T, in
                                     uint64_t sign_seed, float* dst, hipStream_t st) {
     hipLaunchKernelGGL(k_fill_rht, dim3(1), dim3(1), 0, st, dst);
     if (T > 0 && F > 0) {
+        const dim3 g = rht_grid(T, F);
+        const uint32_t tiles = g.x * g.y;
+        const FastDiv tpr = make_fastdiv(g.x);
+        const dim3 grid(tiles < (uint32_t)kRhtAmaxBlocks ? tiles : (uint32_t)kRhtAmaxBlocks);
         if (dt == NVFP4_BF16)
-            hipLaunchKernelGGL(k_rht_amax<uint16_t>, rht_grid(T, F), dim3(kRhtThreads), 0, st,
-                               static_cast<const uint16_t*>(x), T, F, ld, sign_seed, dst);
+            hipLaunchKernelGGL(k_rht_amax<uint16_t>, grid, dim3(kRhtThreads), 0, st,
+                               static_cast<const uint16_t*>(x), T, F, ld, sign_seed, dst, tiles, tpr);
         else
-            hipLaunchKernelGGL(k_rht_amax<float>, rht_grid(T, F), dim3(kRhtThreads), 0, st,
-                               static_cast<const float*>(x), T, F, ld, sign_seed, dst);
+            hipLaunchKernelGGL(k_rht_amax<float>, grid, dim3(kRhtThreads), 0, st,
+                               static_cast<const float*>(x), T, F, ld, sign_seed, dst, tiles, tpr);
     }
     return launch_status();
 }

@@ -56,30 +56,31 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---- per-tensor amax [P3 Come funziona NVFP4?] ------------------------------------------------
-// Grid-stride over groups; one device-scope atomicMax of the float bits per workgroup (the
-// values are non-negative, so their IEEE bit patterns order like the floats).
+// Persistent grid-stride kernel: at most kAmaxBlocks workgroups, each thread keeping
+// kAmaxUnroll 16-byte loads in flight per trip; one device-scope atomicMax of the float bits per
+// workgroup at the end (the values are non-negative, so their bit patterns order like the
+// floats).  Few workgroups keep the number of serialized same-address atomics small.
+constexpr int kAmaxBlocks = 512;
+constexpr int kAmaxUnroll = 8;
+
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 k_amax(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, float* amax_out) {
     float m = 0.0f;
-    const uint32_t stride = gridDim.x * kThreads * kUnroll;
-    for (uint32_t base = blockIdx.x * kThreads * kUnroll + threadIdx.x; base < groups;
+    const uint32_t stride = gridDim.x * kThreads * kAmaxUnroll;
+    for (uint32_t base = blockIdx.x * kThreads * kAmaxUnroll + threadIdx.x; base < groups;
          base += stride) {
-        float y[kUnroll][8];
+        float y[kAmaxUnroll][8];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kAmaxUnroll; ++u) {
             uint32_t g = base + u * kThreads;
-            if (g < groups) {
-                uint32_t row = fastdiv(g, gpr);
-                uint32_t cg = g - row * gpr.d;
-                Group8<T>::load(x + (int64_t)row * ld + cg * 8, y[u]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[u][e] = 0.0f;
-            }
+            g = g < groups ? g : groups - 1;           // clamped duplicate: max is unchanged
+            const uint32_t row = fastdiv(g, gpr);
+            const uint32_t cg = g - row * gpr.d;
+            Group8<T>::load(x + (int64_t)row * ld + cg * 8, y[u]);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kAmaxUnroll; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[u][e]));
     }
@@ -96,9 +97,8 @@ k_amax(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, float*
 }
 
 static int amax_grid(uint32_t groups) {
-    int64_t need = ((int64_t)groups + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-    int64_t cap = 256 * 4;                       // 4 workgroups per CU on 256 CUs
-    return (int)(need < 1 ? 1 : (need < cap ? need : cap));
+    int64_t need = ((int64_t)groups + kThreads * kAmaxUnroll - 1) / (kThreads * kAmaxUnroll);
+    return (int)(need < 1 ? 1 : (need < kAmaxBlocks ? need : kAmaxBlocks));
 }
 
 // ---- 1D quantization [P1 Caracteristicas; P2 Describir] ---------------------------------------
