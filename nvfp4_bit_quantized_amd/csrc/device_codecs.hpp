@@ -34,6 +34,17 @@ __device__ __forceinline__ TensorScales tensor_scales(float A) {
     return t;
 }
 
+// Publish a workgroup's partial amax m >= 0 into the device-wide maximum *dst (which the caller
+// zeroed before the launch).  Non-negative floats order like their bit patterns, so an unsigned
+// atomic max applies; a workgroup whose value cannot raise the current maximum skips the atomic,
+// so that few of the same-address atomics serialize in L2.  A stale read only costs an atomic.
+__device__ __forceinline__ void publish_amax(float* dst, float m) {
+    unsigned int* p = reinterpret_cast<unsigned int*>(dst);
+    const unsigned int v = __float_as_uint(m);
+    if (v > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- E4M3 (OCP E4M3FN), non-negative operands -----------------------------------------------
 // Round to nearest even with saturation at 448 (0x7E); values below 2^-6 use the subnormal
 // quantum 2^-9.  Branch-free: both candidate encodings are formed and one is selected.

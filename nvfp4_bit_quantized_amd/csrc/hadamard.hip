@@ -58,8 +58,8 @@ __device__ __forceinline__ uint32_t rht_sign_mask(uint64_t sign_seed) {
     return philox4x32_10(0u, 0u, 0u, 0u, (uint32_t)sign_seed, (uint32_t)(sign_seed >> 32)).x & 0xFFFFu;
 }
 
-// In place: v <- (1/4) H16 D v with butterflies in the order h = 1, 2, 4, 8.
-__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
+// In place: v <- H16 D v with butterflies in the order h = 1, 2, 4, 8 (no 1/4 factor).
+__device__ __forceinline__ void hd16(float* v, uint32_t sign_mask) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
 #pragma unroll
@@ -71,6 +71,11 @@ __device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
                 v[i] = a + b;
                 v[i + hs] = a - b;
             }
+}
+
+// In place: v <- (1/4) H16 D v.
+__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
+    hd16(v, sign_mask);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
 }
@@ -98,18 +103,24 @@ __device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
     return rc;
 }
 
-// Persistent over (64-feature x 512-token) tiles, at most kRhtAmaxBlocks workgroups, one
-// device-scope atomicMax per workgroup.
-constexpr int kRhtAmaxBlocks = 512;
+// Persistent over (64-feature x 512-token) tiles, at most kRhtAmaxBlocks workgroups, each
+// publishing its maximum once (publish_amax).  The factor 1/4 of the transform is applied to the
+// maximum instead of to every element: scaling by 1/4 and fp32 rounding are both monotonic, so
+// fl(max|t| / 4) = max fl(|t| / 4).
+// A workgroup of kRhtAmaxSub x 256 threads works on kRhtAmaxSub tiles at a time.
+constexpr int kRhtAmaxBlocks = 256;
+constexpr int kRhtAmaxSub = 4;
 
 template <typename T>
-__global__ void __launch_bounds__(kRhtThreads)
+__global__ void __launch_bounds__(kRhtThreads * kRhtAmaxSub)
 k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
            float* amax_out, uint32_t tiles, FastDiv tiles_per_row) {
     const uint32_t mask = rht_sign_mask(sign_seed);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) % (kRhtThreads / 64);
+    const uint32_t sub = threadIdx.x / kRhtThreads;
     float m = 0.0f;
-    for (uint32_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    for (uint32_t tile = blockIdx.x * kRhtAmaxSub + sub; tile < tiles;
+         tile += gridDim.x * kRhtAmaxSub) {
         const uint32_t ty = fastdiv(tile, tiles_per_row), tx = tile - ty * tiles_per_row.d;
         const int64_t f0 = (int64_t)tx * kFeatPerBlock + (lane & 7) * 8;
         const int64_t c = (int64_t)ty * kChunksPerBlock + wave * 8 + (lane >> 3);
@@ -121,7 +132,7 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
                 float v[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[i] = t16.get(i, f);
-                rht16(v, mask);
+                hd16(v, mask);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
             }
@@ -129,14 +140,15 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    __shared__ float part[kRhtThreads / 64];
+    m = 0.25f * m;
+    __shared__ float part[kRhtThreads * kRhtAmaxSub / 64];
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
         float b = part[0];
 #pragma unroll
-        for (int w = 1; w < kRhtThreads / 64; ++w) b = fmaxf(b, part[w]);
-        atomicMax(reinterpret_cast<unsigned int*>(amax_out), __float_as_uint(b));
+        for (int w = 1; w < kRhtThreads * kRhtAmaxSub / 64; ++w) b = fmaxf(b, part[w]);
+        publish_amax(amax_out, b);
     }
 }
 
@@ -216,12 +228,14 @@ static nvfp4_status launch_rht_amax(const void* x, nvfp4_dtype dt, int64_t T, in
         const dim3 g = rht_grid(T, F);
         const uint32_t tiles = g.x * g.y;
         const FastDiv tpr = make_fastdiv(g.x);
-        const dim3 grid(tiles < (uint32_t)kRhtAmaxBlocks ? tiles : (uint32_t)kRhtAmaxBlocks);
+        const uint32_t need = (tiles + kRhtAmaxSub - 1) / kRhtAmaxSub;
+        const dim3 grid(need < (uint32_t)kRhtAmaxBlocks ? need : (uint32_t)kRhtAmaxBlocks);
+        const dim3 block(kRhtThreads * kRhtAmaxSub);
         if (dt == NVFP4_BF16)
-            hipLaunchKernelGGL(k_rht_amax<uint16_t>, grid, dim3(kRhtThreads), 0, st,
+            hipLaunchKernelGGL(k_rht_amax<uint16_t>, grid, block, 0, st,
                                static_cast<const uint16_t*>(x), T, F, ld, sign_seed, dst, tiles, tpr);
         else
-            hipLaunchKernelGGL(k_rht_amax<float>, grid, dim3(kRhtThreads), 0, st,
+            hipLaunchKernelGGL(k_rht_amax<float>, grid, block, 0, st,
                                static_cast<const float*>(x), T, F, ld, sign_seed, dst, tiles, tpr);
     }
     return launch_status();
