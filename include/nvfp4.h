@@ -122,6 +122,29 @@ nvfp4_status nvfp4_hadamard_quantize(const void *x, nvfp4_dtype dt, int64_t ld, 
                                      const float *amax_in, nvfp4_round rnd, uint64_t seed,
                                      const nvfp4_tensor *out, void *stream);
 
+/* amax of x [T x F] and of its random Hadamard transform (as in nvfp4_hadamard_quantize) in one
+ * read of x: *amax_out = max |x|, *amax_t_out = max |(1/4) H16 D x|.  T % 16 == 0, F % 8 == 0;
+ * the two outputs must be distinct (else NVFP4_ERR_SHAPE). */
+nvfp4_status nvfp4_dual_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
+                             uint64_t sign_seed, float *amax_out, float *amax_t_out, void *stream);
+
+/* Fused dual-orientation quantization: one read of an activation or gradient x [T tokens x
+ * F features] (row stride ld) writes both NVFP4 copies a training step takes from it
+ * [P2 Describir: all three GEMMs on FP4 operands; P1 Metodologia: random Hadamard transforms on
+ * the weight-gradient operands]:
+ *   out   [T x F], layout 1x16: the row-wise copy (fprop / dgrad operand), bit-identical to
+ *         nvfp4_quantize_1d(x, dt, ld, amax_in, rnd, seed, out);
+ *   out_t [F x T], layout 1x16: the Hadamard-transformed transposed copy (wgrad operand),
+ *         bit-identical to nvfp4_hadamard_quantize(x, dt, ld, sign_seed, amax_t_in, rnd, seed_t,
+ *         out_t).
+ * amax_in / amax_t_in: the amax of x and of its transform; if either is NULL both are computed
+ * first in one fused pass (nvfp4_dual_amax into out->amax and out_t->amax).  Requirements:
+ * T % 16 == 0, F % 16 == 0; out and out_t have distinct amax and s_dec pointers. */
+nvfp4_status nvfp4_quantize_dual(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
+                                 const float *amax_in, const float *amax_t_in, nvfp4_round rnd,
+                                 uint64_t seed, uint64_t seed_t, const nvfp4_tensor *out,
+                                 const nvfp4_tensor *out_t, void *stream);
+
 /* Dequantize an NVFP4 tensor (1x16 or 16x16): y = fl(fl(v * scale_b) * s_dec) in fp32, stored
  * as fp32 or rounded to nearest-even bf16.  y is [q->rows x q->cols], row stride ld. */
 nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dtype dt, int64_t ld,

@@ -22,7 +22,7 @@ BLK_1x16, BLK_16x16, MX_1x32 = 0, 1, 2
 
 SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_quantize_1d",
            "nvfp4_quantize_2d", "nvfp4_hadamard_quantize", "nvfp4_dequantize", "nvfp4_gemm",
-           "mxfp4_quantize_1d", "mxfp4_gemm")
+           "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual")
 
 
 class NvTensor(C.Structure):
@@ -55,6 +55,8 @@ def lib():
         L.nvfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.mxfp4_quantize_1d.argtypes = [P, i32, i64, i32, u64, T, P]
         L.mxfp4_gemm.argtypes = [T, T, P, i32, i64, P]
+        L.nvfp4_dual_amax.argtypes = [P, i32, i64, i64, i64, u64, P, P, P]
+        L.nvfp4_quantize_dual.argtypes = [P, i32, i64, u64, P, P, i32, u64, u64, T, T, P]
         for name in SYMBOLS[1:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -179,6 +181,35 @@ def hadamard_quantize(x: torch.Tensor, sign_seed: int, rounding: int = RNE, seed
            lib().nvfp4_hadamard_quantize(_ptr(x), dt, ld, sign_seed, _ptr(amax_in), rounding, seed,
                                          C.byref(d), _stream(x.device)))
     return q
+
+
+def dual_amax(x: torch.Tensor, sign_seed: int, out: torch.Tensor | None = None,
+              out_t: torch.Tensor | None = None):
+    """(amax of x, amax of its random Hadamard transform) from one read of x [T x F]."""
+    x, dt, ld = _x(x)
+    out = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
+    out_t = torch.empty(1, dtype=torch.float32, device=x.device) if out_t is None else out_t
+    _check("nvfp4_dual_amax", lib().nvfp4_dual_amax(_ptr(x), dt, x.shape[0], x.shape[1], ld,
+                                                    sign_seed, _ptr(out), _ptr(out_t),
+                                                    _stream(x.device)))
+    return out, out_t
+
+
+def quantize_dual(x: torch.Tensor, sign_seed: int, rounding: int = RNE, seed: int = 0,
+                  seed_t: int = 0, amax_in: torch.Tensor | None = None,
+                  amax_t_in: torch.Tensor | None = None, out: QTensor | None = None,
+                  out_t: QTensor | None = None):
+    """x [T x F] -> (row-wise NVFP4 [T x F], Hadamard-transformed NVFP4 [F x T]) from one read."""
+    x, dt, ld = _x(x)
+    T, F = x.shape
+    q = QTensor.empty(T, F, BLK_1x16, x.device) if out is None else out
+    qt = QTensor.empty(F, T, BLK_1x16, x.device) if out_t is None else out_t
+    d, dt_ = q.desc(), qt.desc()
+    _check("nvfp4_quantize_dual",
+           lib().nvfp4_quantize_dual(_ptr(x), dt, ld, sign_seed, _ptr(amax_in), _ptr(amax_t_in),
+                                     rounding, seed, seed_t, C.byref(d), C.byref(dt_),
+                                     _stream(x.device)))
+    return q, qt
 
 
 def dequantize(q: QTensor, dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None):

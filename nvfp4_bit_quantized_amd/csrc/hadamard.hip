@@ -80,8 +80,6 @@ __device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
     for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
 }
 
-__global__ void k_fill_rht(float* p) { *p = 0.0f; }
-
 __global__ void k_scalars_rht(const float* src, float* amax_out, float* sdec_out) {
     const float A = *src;
     *amax_out = A;
@@ -107,18 +105,19 @@ __device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
 // publishing its maximum once (publish_amax).  The factor 1/4 of the transform is applied to the
 // maximum instead of to every element: scaling by 1/4 and fp32 rounding are both monotonic, so
 // fl(max|t| / 4) = max fl(|t| / 4).
-// A workgroup of kRhtAmaxSub x 256 threads works on kRhtAmaxSub tiles at a time.
+// A workgroup of kRhtAmaxSub x 256 threads works on kRhtAmaxSub tiles at a time.  With kPlain
+// the same pass also takes the amax of x itself (for the fused dual-orientation quantizer).
 constexpr int kRhtAmaxBlocks = 256;
 constexpr int kRhtAmaxSub = 4;
 
-template <typename T>
+template <typename T, bool kPlain>
 __global__ void __launch_bounds__(kRhtThreads * kRhtAmaxSub)
 k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
-           float* amax_out, uint32_t tiles, FastDiv tiles_per_row) {
+           float* amax_out, float* amax_plain_out, uint32_t tiles, FastDiv tiles_per_row) {
     const uint32_t mask = rht_sign_mask(sign_seed);
     const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) % (kRhtThreads / 64);
     const uint32_t sub = threadIdx.x / kRhtThreads;
-    float m = 0.0f;
+    float m = 0.0f, mp = 0.0f;
     for (uint32_t tile = blockIdx.x * kRhtAmaxSub + sub; tile < tiles;
          tile += gridDim.x * kRhtAmaxSub) {
         const uint32_t ty = fastdiv(tile, tiles_per_row), tx = tile - ty * tiles_per_row.d;
@@ -132,6 +131,10 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
                 float v[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[i] = t16.get(i, f);
+                if constexpr (kPlain) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) mp = fmaxf(mp, fabsf(v[i]));
+                }
                 hd16(v, mask);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -139,35 +142,38 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
         }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    for (int off = 32; off >= 1; off >>= 1) {
+        m = fmaxf(m, __shfl_xor(m, off));
+        if constexpr (kPlain) mp = fmaxf(mp, __shfl_xor(mp, off));
+    }
     m = 0.25f * m;
-    __shared__ float part[kRhtThreads * kRhtAmaxSub / 64];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    constexpr int kWaves = kRhtThreads * kRhtAmaxSub / 64;
+    __shared__ float part[2][kWaves];
+    if ((threadIdx.x & 63) == 0) {
+        part[0][threadIdx.x >> 6] = m;
+        part[1][threadIdx.x >> 6] = mp;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        float b = part[0];
+        float b = part[0][0], bp = part[1][0];
 #pragma unroll
-        for (int w = 1; w < kRhtThreads * kRhtAmaxSub / 64; ++w) b = fmaxf(b, part[w]);
+        for (int w = 1; w < kWaves; ++w) {
+            b = fmaxf(b, part[0][w]);
+            bp = fmaxf(bp, part[1][w]);
+        }
         publish_amax(amax_out, b);
+        if constexpr (kPlain) publish_amax(amax_plain_out, bp);
     }
 }
 
+// The transposed copy of one thread's tile: for each of its 8 features, the 16 tokens of its
+// chunk through (1/4) H16 D, one NVFP4 block of row `feature` of the [F x T] output.
 template <typename T, bool kSR>
-__global__ void __launch_bounds__(kRhtThreads)
-k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
-            const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
-            uint8_t* __restrict__ scales, float* amax_out, float* sdec_out) {
-    const float A = *amax_src;
-    const TensorScales ts = tensor_scales(A);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-        *amax_out = A;
-        *sdec_out = ts.s_dec;
-    }
-    const RhtCoords rc = rht_coords(Tn, F);
-    if (!rc.valid) return;
-    const uint32_t mask = rht_sign_mask(sign_seed);
-    Tile16x8<T> tile;
-    tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+__device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, const RhtCoords& rc,
+                                                      int64_t Tn, int64_t F, uint32_t mask,
+                                                      const TensorScales& ts, uint64_t seed,
+                                                      uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
         const int64_t feat = rc.f0 + f;
@@ -208,6 +214,99 @@ k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t
     }
 }
 
+// The row-wise copy of one thread's tile: for each of its 16 token rows, its 8 features are one
+// half of a 16-feature NVFP4 block whose other half sits in the adjacent lane (lane ^ 1, which
+// holds the same rows and the next or previous 8 features); the block amax is shared with one
+// DPP lane swap and the even lane writes the scale byte.  F % 16 == 0, so both lanes of a pair
+// are valid or neither is.
+template <typename T, bool kSR>
+__device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const RhtCoords& rc,
+                                                int64_t F, const TensorScales& ts, uint64_t seed,
+                                                uint8_t* __restrict__ codes,
+                                                uint8_t* __restrict__ scales) {
+    const bool lead = (threadIdx.x & 1) == 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float y[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) y[f] = tile.get(i, f);
+        float m = 0.0f;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) m = fmaxf(m, fabsf(y[f]));
+        m = fmaxf(m, swap_adjacent(m));
+        uint32_t sb;
+        float enc;
+        block_scale(m, ts, sb, enc);
+        const int64_t row = rc.c * 16 + i;
+        uint32_t packed;
+        if constexpr (kSR) {
+            const u32x4 w = sr_words(seed, (uint64_t)row * (uint64_t)F + (uint64_t)rc.f0);
+            const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+            float z[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ze = y[e] * enc;
+                z[e] = ze + ze;
+            }
+            packed = e2m1_sr_pack8(z, words);
+        } else {
+            float z[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = y[e] * enc;
+            packed = e2m1_rne_pack8(z);
+        }
+        *reinterpret_cast<uint32_t*>(codes + row * (F / 2) + rc.f0 / 2) = packed;
+        if (lead) scales[row * (F / 16) + rc.f0 / 16] = (uint8_t)sb;
+    }
+}
+
+template <typename T, bool kSR>
+__global__ void __launch_bounds__(kRhtThreads)
+k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
+            const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
+            uint8_t* __restrict__ scales, float* amax_out, float* sdec_out) {
+    const float A = *amax_src;
+    const TensorScales ts = tensor_scales(A);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        *amax_out = A;
+        *sdec_out = ts.s_dec;
+    }
+    const RhtCoords rc = rht_coords(Tn, F);
+    if (!rc.valid) return;
+    const uint32_t mask = rht_sign_mask(sign_seed);
+    Tile16x8<T> tile;
+    tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+    quant_tile_transposed<T, kSR>(tile, rc, Tn, F, mask, ts, seed, codes, scales);
+}
+
+// Fused dual-orientation quantizer: one read of x gives the row-wise copy [T x F] (as the 1D
+// quantizer makes it, element index row * F + col for SR) and the Hadamard-transformed
+// transposed copy [F x T] (as k_rht_quant makes it, element index feature * T + token).
+template <typename T, bool kSR>
+__global__ void __launch_bounds__(kRhtThreads)
+k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
+             const float* __restrict__ amax_src, const float* __restrict__ amax_t_src,
+             uint64_t seed, uint64_t seed_t, uint8_t* __restrict__ codes,
+             uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
+             uint8_t* __restrict__ scales_t, float* amax_out, float* sdec_out, float* amax_t_out,
+             float* sdec_t_out) {
+    const float A = *amax_src, At = *amax_t_src;
+    const TensorScales ts = tensor_scales(A), tst = tensor_scales(At);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        *amax_out = A;
+        *sdec_out = ts.s_dec;
+        *amax_t_out = At;
+        *sdec_t_out = tst.s_dec;
+    }
+    const RhtCoords rc = rht_coords(Tn, F);
+    if (!rc.valid) return;
+    const uint32_t mask = rht_sign_mask(sign_seed);
+    Tile16x8<T> tile;
+    tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+    quant_tile_rows<T, kSR>(tile, rc, F, ts, seed, codes, scales);
+    quant_tile_transposed<T, kSR>(tile, rc, Tn, F, mask, tst, seed_t, codes_t, scales_t);
+}
+
 static dim3 rht_grid(int64_t T, int64_t F) {
     return dim3((unsigned)((F + kFeatPerBlock - 1) / kFeatPerBlock),
                 (unsigned)((T / 16 + kChunksPerBlock - 1) / kChunksPerBlock));
@@ -221,9 +320,17 @@ static nvfp4_status check_rht_input(const void* x, nvfp4_dtype dt, int64_t T, in
     return NVFP4_OK;
 }
 
+__global__ void k_fill2_rht(float* p, float* q) {
+    *p = 0.0f;
+    if (q) *q = 0.0f;
+}
+
+// The amax of the transformed tensor into *dst and, if plain_dst is non-NULL, the amax of x
+// itself into *plain_dst, in one pass.
 static nvfp4_status launch_rht_amax(const void* x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
-                                    uint64_t sign_seed, float* dst, hipStream_t st) {
-    hipLaunchKernelGGL(k_fill_rht, dim3(1), dim3(1), 0, st, dst);
+                                    uint64_t sign_seed, float* dst, float* plain_dst,
+                                    hipStream_t st) {
+    hipLaunchKernelGGL(k_fill2_rht, dim3(1), dim3(1), 0, st, dst, plain_dst);
     if (T > 0 && F > 0) {
         const dim3 g = rht_grid(T, F);
         const uint32_t tiles = g.x * g.y;
@@ -231,14 +338,23 @@ static nvfp4_status launch_rht_amax(const void* x, nvfp4_dtype dt, int64_t T, in
         const uint32_t need = (tiles + kRhtAmaxSub - 1) / kRhtAmaxSub;
         const dim3 grid(need < (uint32_t)kRhtAmaxBlocks ? need : (uint32_t)kRhtAmaxBlocks);
         const dim3 block(kRhtThreads * kRhtAmaxSub);
-        if (dt == NVFP4_BF16)
-            hipLaunchKernelGGL(k_rht_amax<uint16_t>, grid, block, 0, st,
-                               static_cast<const uint16_t*>(x), T, F, ld, sign_seed, dst, tiles, tpr);
-        else
-            hipLaunchKernelGGL(k_rht_amax<float>, grid, block, 0, st,
-                               static_cast<const float*>(x), T, F, ld, sign_seed, dst, tiles, tpr);
+#define NVFP4_RA(TT, PLAIN)                                                                       \
+        hipLaunchKernelGGL((k_rht_amax<TT, PLAIN>), grid, block, 0, st, static_cast<const TT*>(x), \
+                           T, F, ld, sign_seed, dst, plain_dst, tiles, tpr)
+        if (dt == NVFP4_BF16) {
+            if (plain_dst) NVFP4_RA(uint16_t, true); else NVFP4_RA(uint16_t, false);
+        } else {
+            if (plain_dst) NVFP4_RA(float, true); else NVFP4_RA(float, false);
+        }
+#undef NVFP4_RA
     }
     return launch_status();
+}
+
+static nvfp4_status check_amax_ptr(const float* p) {
+    if (!p) return NVFP4_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
 }
 
 }  // namespace nvfp4
@@ -250,9 +366,19 @@ extern "C" nvfp4_status nvfp4_hadamard_amax(const void* x, nvfp4_dtype dt, int64
                                             void* stream) {
     nvfp4_status s = check_rht_input(x, dt, T, F, ld);
     if (s) return s;
-    if (!amax_out) return NVFP4_ERR_NULL;
-    if (reinterpret_cast<uintptr_t>(amax_out) & 3u) return NVFP4_ERR_ALIGN;
-    return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_out, as_stream(stream));
+    s = check_amax_ptr(amax_out);
+    if (s) return s;
+    return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_out, nullptr, as_stream(stream));
+}
+
+extern "C" nvfp4_status nvfp4_dual_amax(const void* x, nvfp4_dtype dt, int64_t T, int64_t F,
+                                        int64_t ld, uint64_t sign_seed, float* amax_out,
+                                        float* amax_t_out, void* stream) {
+    nvfp4_status s = check_rht_input(x, dt, T, F, ld);
+    if (s) return s;
+    if ((s = check_amax_ptr(amax_out)) || (s = check_amax_ptr(amax_t_out))) return s;
+    if (amax_out == amax_t_out) return NVFP4_ERR_SHAPE;
+    return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_t_out, amax_out, as_stream(stream));
 }
 
 extern "C" nvfp4_status nvfp4_hadamard_quantize(const void* x, nvfp4_dtype dt, int64_t ld,
@@ -268,7 +394,7 @@ extern "C" nvfp4_status nvfp4_hadamard_quantize(const void* x, nvfp4_dtype dt, i
     hipStream_t st = as_stream(stream);
     const float* src = amax_in;
     if (!src) {
-        s = launch_rht_amax(x, dt, T, F, ld, sign_seed, out->amax, st);
+        s = launch_rht_amax(x, dt, T, F, ld, sign_seed, out->amax, nullptr, st);
         if (s) return s;
         src = out->amax;
     }
@@ -286,5 +412,51 @@ extern "C" nvfp4_status nvfp4_hadamard_quantize(const void* x, nvfp4_dtype dt, i
         if (rnd == NVFP4_SR) NVFP4_RQ(float, true); else NVFP4_RQ(float, false);
     }
 #undef NVFP4_RQ
+    return launch_status();
+}
+
+extern "C" nvfp4_status nvfp4_quantize_dual(const void* x, nvfp4_dtype dt, int64_t ld,
+                                            uint64_t sign_seed, const float* amax_in,
+                                            const float* amax_t_in, nvfp4_round rnd,
+                                            uint64_t seed, uint64_t seed_t,
+                                            const nvfp4_tensor* out, const nvfp4_tensor* out_t,
+                                            void* stream) {
+    nvfp4_status s = check_q(out, NVFP4_BLK_1x16, true);
+    if (s) return s;
+    s = check_q(out_t, NVFP4_BLK_1x16, true);
+    if (s) return s;
+    const int64_t T = out->rows, F = out->cols;
+    if (out_t->rows != F || out_t->cols != T) return NVFP4_ERR_SHAPE;
+    s = check_rht_input(x, dt, T, F, ld);
+    if (s) return s;
+    if (F % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
+    if (out->amax == out_t->amax || out->s_dec == out_t->s_dec) return NVFP4_ERR_SHAPE;
+    hipStream_t st = as_stream(stream);
+    const float* src = amax_in;
+    const float* src_t = amax_t_in;
+    if (!src || !src_t) {
+        s = launch_rht_amax(x, dt, T, F, ld, sign_seed, out_t->amax, out->amax, st);
+        if (s) return s;
+        if (!src) src = out->amax;
+        if (!src_t) src_t = out_t->amax;
+    }
+    if (T == 0 || F == 0) {
+        hipLaunchKernelGGL(k_scalars_rht, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
+        hipLaunchKernelGGL(k_scalars_rht, dim3(1), dim3(1), 0, st, src_t, out_t->amax, out_t->s_dec);
+        return launch_status();
+    }
+    const dim3 grid = rht_grid(T, F), block(kRhtThreads);
+#define NVFP4_DQ(TT, SRV)                                                                         \
+    hipLaunchKernelGGL((k_dual_quant<TT, SRV>), grid, block, 0, st, static_cast<const TT*>(x), T, \
+                       F, ld, sign_seed, src, src_t, seed, seed_t, out->codes, out->scales,        \
+                       out_t->codes, out_t->scales, out->amax, out->s_dec, out_t->amax,            \
+                       out_t->s_dec)
+    if (dt == NVFP4_BF16) {
+        if (rnd == NVFP4_SR) NVFP4_DQ(uint16_t, true); else NVFP4_DQ(uint16_t, false);
+    } else {
+        if (rnd == NVFP4_SR) NVFP4_DQ(float, true); else NVFP4_DQ(float, false);
+    }
+#undef NVFP4_DQ
     return launch_status();
 }

@@ -101,3 +101,27 @@ def test_dequantize_validation(L):
     assert L.nvfp4_dequantize(None, FAKE, nv.F32, 32, None) == nv.ERR_NULL
     bad = _q(16, 32, layout=7)
     assert L.nvfp4_dequantize(C.byref(bad), FAKE, nv.F32, 32, None) == nv.ERR_LAYOUT
+
+
+def test_dual_validation(L):
+    assert L.nvfp4_dual_amax(FAKE, nv.BF16, 40, 16, 16, 1, FAKE, FAKE + 4, None) == nv.ERR_SHAPE
+    assert L.nvfp4_dual_amax(FAKE, nv.BF16, 32, 16, 16, 1, None, FAKE, None) == nv.ERR_NULL
+    assert L.nvfp4_dual_amax(FAKE, nv.BF16, 32, 16, 16, 1, FAKE, FAKE, None) == nv.ERR_SHAPE
+    assert L.nvfp4_dual_amax(FAKE, nv.BF16, 32, 16, 16, 1, FAKE, FAKE + 2, None) == nv.ERR_ALIGN
+    q, qt = _q(32, 48), _q(48, 32, amax=FAKE + 4, sdec=FAKE + 8)
+    assert L.nvfp4_quantize_dual(FAKE, nv.BF16, 48, 1, None, None, nv.RNE, 0, 0, C.byref(q),
+                                 None, None) == nv.ERR_NULL
+    assert L.nvfp4_quantize_dual(FAKE, nv.BF16, 48, 1, None, None, 5, 0, 0, C.byref(q),
+                                 C.byref(qt), None) == nv.ERR_DTYPE
+    wrong = _q(32, 32, amax=FAKE + 4, sdec=FAKE + 8)
+    assert L.nvfp4_quantize_dual(FAKE, nv.BF16, 48, 1, None, None, nv.RNE, 0, 0, C.byref(q),
+                                 C.byref(wrong), None) == nv.ERR_SHAPE
+    same = _q(48, 32)
+    assert L.nvfp4_quantize_dual(FAKE, nv.BF16, 48, 1, None, None, nv.RNE, 0, 0, C.byref(q),
+                                 C.byref(same), None) == nv.ERR_SHAPE
+    mx = _q(48, 32, layout=nv.MX_1x32, amax=FAKE + 4, sdec=FAKE + 8)
+    assert L.nvfp4_quantize_dual(FAKE, nv.BF16, 48, 1, None, None, nv.RNE, 0, 0, C.byref(q),
+                                 C.byref(mx), None) == nv.ERR_LAYOUT
+    assert L.nvfp4_quantize_dual(FAKE + 2, nv.BF16, 48, 1, None, None, nv.RNE, 0, 0, C.byref(q),
+                                 C.byref(qt), None) == nv.ERR_ALIGN
+
