@@ -101,6 +101,20 @@ nvfp4_status nvfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, const 
                                nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
                                void *stream);
 
+/* nvfp4_quantize_1d plus, in the same pass, the quantization-noise diagnostic of
+ * [P2 Describir: quantized training loses efficiency once the gradient norm falls below about
+ * sqrt(3) times the quantization noise]: sums[0] = sum of x^2 and sums[1] = sum of (Q(x) - x)^2
+ * over the tensor, Q(x) the dequantized value (as nvfp4_dequantize computes it in fp32).  The
+ * gradient norm is sqrt(sums[0]), the noise sqrt(sums[1]); the caller compares their ratio with
+ * sqrt(3).  sums: device, two doubles, 8-byte aligned, overwritten.  Accumulated in fp32 per
+ * 16-element block (on values times s_enc = 2688 / amax) and in fp64 across blocks, with device
+ * atomics: the order of the additions, and so the last bits of the sums, vary from run to run;
+ * codes and scales are exactly those of nvfp4_quantize_1d.  A tensor treated as zero (amax below
+ * 2^-100) reports sums of its fp32 squares, which may underflow to 0. */
+nvfp4_status nvfp4_quantize_1d_noise(const void *x, nvfp4_dtype dt, int64_t ld, const float *amax_in,
+                                     nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
+                                     double *sums, void *stream);
+
 /* 2D NVFP4 quantization of a weight w [out->rows x out->cols] with one E4M3 scale per 16x16
  * tile, round to nearest [P1 Metodologia: two-dimensional block scaling for weights].
  * out: layout NVFP4_BLK_16x16, rows % 16 == cols % 16 == 0.  out_t (optional, may be NULL):

@@ -22,7 +22,8 @@ BLK_1x16, BLK_16x16, MX_1x32 = 0, 1, 2
 
 SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_quantize_1d",
            "nvfp4_quantize_2d", "nvfp4_hadamard_quantize", "nvfp4_dequantize", "nvfp4_gemm",
-           "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual")
+           "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual",
+           "nvfp4_quantize_1d_noise")
 
 
 class NvTensor(C.Structure):
@@ -57,6 +58,7 @@ def lib():
         L.mxfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.nvfp4_dual_amax.argtypes = [P, i32, i64, i64, i64, u64, P, P, P]
         L.nvfp4_quantize_dual.argtypes = [P, i32, i64, u64, P, P, i32, u64, u64, T, T, P]
+        L.nvfp4_quantize_1d_noise.argtypes = [P, i32, i64, P, i32, u64, T, P, P]
         for name in SYMBOLS[1:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -152,6 +154,30 @@ def quantize_1d(x: torch.Tensor, rounding: int = RNE, seed: int = 0,
     _check("nvfp4_quantize_1d", lib().nvfp4_quantize_1d(_ptr(x), dt, ld, _ptr(amax_in), rounding,
                                                         seed, C.byref(d), _stream(x.device)))
     return q
+
+
+def quantize_1d_noise(x: torch.Tensor, rounding: int = SR, seed: int = 0,
+                      amax_in: torch.Tensor | None = None, out: QTensor | None = None,
+                      sums: torch.Tensor | None = None):
+    """quantize_1d plus the noise diagnostic: (QTensor, sums) with sums a device float64 [2] =
+    (sum x^2, sum (Q(x) - x)^2).  ``noise_report(sums)`` turns it into norms and the ratio."""
+    x, dt, ld = _x(x)
+    q = QTensor.empty(x.shape[0], x.shape[1], BLK_1x16, x.device) if out is None else out
+    sums = torch.empty(2, dtype=torch.float64, device=x.device) if sums is None else sums
+    d = q.desc()
+    _check("nvfp4_quantize_1d_noise",
+           lib().nvfp4_quantize_1d_noise(_ptr(x), dt, ld, _ptr(amax_in), rounding, seed,
+                                         C.byref(d), _ptr(sums), _stream(x.device)))
+    return q, sums
+
+
+def noise_report(sums: torch.Tensor) -> dict:
+    """Norms and ratio from the two sums: quantized training is flagged as inefficient when
+    ||g|| < sqrt(3) * ||Q(g) - g||."""
+    g2, e2 = (float(v) for v in sums.cpu().tolist())
+    g, e = g2 ** 0.5, e2 ** 0.5
+    ratio = g / e if e > 0 else float("inf")
+    return {"grad_norm": g, "noise_norm": e, "ratio": ratio, "below_sqrt3": ratio < 3 ** 0.5}
 
 
 def quantize_2d(w: torch.Tensor, transposed: bool = True, amax_in: torch.Tensor | None = None,

@@ -102,15 +102,34 @@ static int amax_grid(uint32_t groups) {
     return (int)(need < 1 ? 1 : (need < kAmaxBlocks ? need : kAmaxBlocks));
 }
 
+// Values of eight packed E2M1 codes (element 2j in the low nibble of byte j); with a unit scale
+// v_cvt_scalef32_pk_f32_fp4 returns the exact E2M1 values.
+__device__ __forceinline__ void e2m1_decode8(uint32_t w, float* v) {
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+}
+
 // ---- 1D quantization [P1 Caracteristicas; P2 Describir] ---------------------------------------
 // One lane owns one whole 16-element block: two 16-byte loads (bf16), one 8-byte code store and
 // one scale byte.  Each thread handles kQUnroll blocks spaced a workgroup apart, all loads first.
 // Blocks past the end load a clamped (valid) block and store nothing.
-template <typename T, bool kSR>
+//
+// With kNoise the same pass also accumulates the quantization-noise diagnostic
+// [P2 Describir: quantized training loses efficiency once the gradient norm falls below about
+// sqrt(3) times the quantization noise]: sums[0] += x^2 and sums[1] += (Q(x) - x)^2, where
+// Q(x) = fl(fl(v * scale) * s_dec) is the dequantized value.  The squares are taken of the
+// values times s_enc = 2688 / amax (at most 5376 in magnitude, so no fp32 overflow or early
+// underflow), each 16-element block is summed in fp32, blocks are accumulated in fp64, and each
+// workgroup adds its two totals, divided by s_enc^2, atomically.
+template <typename T, bool kSR, bool kNoise>
 __global__ void __launch_bounds__(kThreads)
 k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uint32_t cols,
           const float* __restrict__ amax_src, uint64_t seed, uint2* __restrict__ codes,
-          uint8_t* __restrict__ scales, float* amax_out, float* sdec_out) {
+          uint8_t* __restrict__ scales, float* amax_out, float* sdec_out, double* sums) {
     const float A = *amax_src;
     const TensorScales ts = tensor_scales(A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -120,6 +139,7 @@ k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uin
     const uint32_t base = blockIdx.x * kThreads * kQUnroll + threadIdx.x;
     float y[kQUnroll][16];
     uint32_t row[kQUnroll], cb[kQUnroll];
+    double g2 = 0.0, e2 = 0.0;
 #pragma unroll
     for (int u = 0; u < kQUnroll; ++u) {
         uint32_t b = base + u * kThreads;
@@ -162,8 +182,53 @@ k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uin
         if (b < blocks) {
             codes[b] = make_uint2(lo, hi);       // blocks are dense in the code array
             scales[b] = (uint8_t)sb;
+            if constexpr (kNoise) {
+                const float sc = e4m3_decode(sb);
+                float v[16];
+                e2m1_decode8(lo, v);
+                e2m1_decode8(hi, v + 8);
+                float bg = 0.0f, be = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float d = (v[e] * sc) * ts.s_dec - y[u][e];
+                    const float ys = y[u][e] * ts.s_enc, ds = d * ts.s_enc;   // |.| <= 5376
+                    bg += ys * ys;
+                    be += ds * ds;
+                }
+                g2 += (double)bg;
+                e2 += (double)be;
+            }
         }
     }
+    if constexpr (kNoise) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            g2 += __shfl_xor(g2, off);
+            e2 += __shfl_xor(e2, off);
+        }
+        __shared__ double part[2][kThreads / 64];
+        if ((threadIdx.x & 63) == 0) {
+            part[0][threadIdx.x >> 6] = g2;
+            part[1][threadIdx.x >> 6] = e2;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double a = 0.0, c = 0.0;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w) {
+                a += part[0][w];
+                c += part[1][w];
+            }
+            const double inv = 1.0 / ((double)ts.s_enc * (double)ts.s_enc);
+            atomicAdd(sums, a * inv);
+            atomicAdd(sums + 1, c * inv);
+        }
+    }
+}
+
+__global__ void k_fill_f64x2(double* p) {
+    p[0] = 0.0;
+    p[1] = 0.0;
 }
 
 // ---- 2D quantization of weights [P1 Metodologia: two-dimensional block scaling] ---------------
@@ -406,22 +471,22 @@ extern "C" nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, 
     return launch_amax(x, dt, rows, cols, ld, amax_out, as_stream(stream));
 }
 
-extern "C" nvfp4_status nvfp4_quantize_1d(const void* x, nvfp4_dtype dt, int64_t ld,
-                                          const float* amax_in, nvfp4_round rnd, uint64_t seed,
-                                          const nvfp4_tensor* out, void* stream) {
+static nvfp4_status quantize_1d(const void* x, nvfp4_dtype dt, int64_t ld, const float* amax_in,
+                                nvfp4_round rnd, uint64_t seed, const nvfp4_tensor* out,
+                                double* sums, hipStream_t st) {
     nvfp4_status s = check_q(out, NVFP4_BLK_1x16, true);
     if (s) return s;
     s = check_input(x, dt, out->rows, out->cols, ld);
     if (s) return s;
     if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
     if (too_big(out->rows, out->cols)) return NVFP4_ERR_SHAPE;
-    hipStream_t st = as_stream(stream);
     const float* src = amax_in;
     if (!src) {
         s = launch_amax(x, dt, out->rows, out->cols, ld, out->amax, st);
         if (s) return s;
         src = out->amax;
     }
+    if (sums) hipLaunchKernelGGL(k_fill_f64x2, dim3(1), dim3(1), 0, st, sums);
     const uint32_t blocks = (uint32_t)(out->rows * (out->cols / 16));
     if (blocks == 0) {
         hipLaunchKernelGGL(k_tensor_scalars, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
@@ -431,16 +496,35 @@ extern "C" nvfp4_status nvfp4_quantize_1d(const void* x, nvfp4_dtype dt, int64_t
     const dim3 grid(stream_grid(blocks, kQUnroll)), block(kThreads);
     uint2* codes = reinterpret_cast<uint2*>(out->codes);
     const uint32_t cols = (uint32_t)out->cols;
-#define NVFP4_Q1(T, SRV)                                                                         \
-    hipLaunchKernelGGL((k_quant1d<T, SRV>), grid, block, 0, st, static_cast<const T*>(x), ld,     \
-                       blocks, bpr, cols, src, seed, codes, out->scales, out->amax, out->s_dec)
+#define NVFP4_Q1(T, SRV, NZ)                                                                     \
+    hipLaunchKernelGGL((k_quant1d<T, SRV, NZ>), grid, block, 0, st, static_cast<const T*>(x), ld, \
+                       blocks, bpr, cols, src, seed, codes, out->scales, out->amax, out->s_dec,   \
+                       sums)
+#define NVFP4_Q1R(T, NZ)                                                                          \
+    if (rnd == NVFP4_SR) NVFP4_Q1(T, true, NZ); else NVFP4_Q1(T, false, NZ)
     if (dt == NVFP4_BF16) {
-        if (rnd == NVFP4_SR) NVFP4_Q1(uint16_t, true); else NVFP4_Q1(uint16_t, false);
+        if (sums) NVFP4_Q1R(uint16_t, true); else NVFP4_Q1R(uint16_t, false);
     } else {
-        if (rnd == NVFP4_SR) NVFP4_Q1(float, true); else NVFP4_Q1(float, false);
+        if (sums) NVFP4_Q1R(float, true); else NVFP4_Q1R(float, false);
     }
+#undef NVFP4_Q1R
 #undef NVFP4_Q1
     return launch_status();
+}
+
+extern "C" nvfp4_status nvfp4_quantize_1d(const void* x, nvfp4_dtype dt, int64_t ld,
+                                          const float* amax_in, nvfp4_round rnd, uint64_t seed,
+                                          const nvfp4_tensor* out, void* stream) {
+    return quantize_1d(x, dt, ld, amax_in, rnd, seed, out, nullptr, as_stream(stream));
+}
+
+extern "C" nvfp4_status nvfp4_quantize_1d_noise(const void* x, nvfp4_dtype dt, int64_t ld,
+                                                const float* amax_in, nvfp4_round rnd,
+                                                uint64_t seed, const nvfp4_tensor* out,
+                                                double* sums, void* stream) {
+    if (!sums) return NVFP4_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(sums) & 7u) return NVFP4_ERR_ALIGN;
+    return quantize_1d(x, dt, ld, amax_in, rnd, seed, out, sums, as_stream(stream));
 }
 
 extern "C" nvfp4_status nvfp4_quantize_2d(const void* w, nvfp4_dtype dt, int64_t ld,

@@ -282,6 +282,24 @@ def dequantize(q: dict, rows: int, cols: int, out_bf16: bool = False) -> np.ndar
     return out
 
 
+def values(x: np.ndarray) -> np.ndarray:
+    """float64 values of a float32 array or of raw bf16 bits (the upper half of an fp32)."""
+    x, dt = _input(x)
+    if dt == BF16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def quant_noise(x: np.ndarray, q: dict) -> tuple[float, float]:
+    """Quantization-noise diagnostic ("FP4 All the Way", Describir: quantized training loses
+    efficiency once the gradient norm falls below about sqrt(3) times the quantization noise):
+    (sum x^2, sum (Q(x) - x)^2) in float64, with Q(x) the dequantized tensor (``dequantize``)."""
+    xv = values(x)
+    rows, cols = xv.shape
+    qv = dequantize(q, rows, cols).astype(np.float64)
+    return float(np.sum(xv * xv)), float(np.sum((qv - xv) ** 2))
+
+
 def gemm_f64(a: dict, b: dict, M: int, N: int, K: int, rows: np.ndarray | None = None) -> np.ndarray:
     """C = A * B^T in float64 for the selected rows of A (all rows if None)."""
     rsel = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)

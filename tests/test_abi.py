@@ -125,3 +125,13 @@ def test_dual_validation(L):
     assert L.nvfp4_quantize_dual(FAKE + 2, nv.BF16, 48, 1, None, None, nv.RNE, 0, 0, C.byref(q),
                                  C.byref(qt), None) == nv.ERR_ALIGN
 
+
+def test_noise_validation(L):
+    q = _q(8, 32)
+    assert L.nvfp4_quantize_1d_noise(FAKE, nv.BF16, 32, None, nv.SR, 0, C.byref(q), None,
+                                     None) == nv.ERR_NULL
+    assert L.nvfp4_quantize_1d_noise(FAKE, nv.BF16, 32, None, nv.SR, 0, C.byref(q), FAKE + 4,
+                                     None) == nv.ERR_ALIGN
+    assert L.nvfp4_quantize_1d_noise(FAKE, nv.BF16, 16, None, nv.SR, 0, C.byref(q), FAKE,
+                                     None) == nv.ERR_SHAPE
+
