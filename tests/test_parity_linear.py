@@ -1,0 +1,133 @@
+"""The NVFP4 linear layer (autograd Function over the C ABI) against the CPU oracle, the BF16
+flag against torch's linear, and an FFN pair against its BF16 counterpart (numeric error only).
+
+Parity: y = x W^T, dx = dy W and dW = dy^T x from the layer must match the oracle's float64 GEMMs
+on the oracle's own quantized operands (1D RNE for x, 16x16 tiles for W and its transposed copy,
+1D SR for dy at the dgrad seed, random-Hadamard RNE/SR transposed copies of x and dy at the
+wgrad seed) within relative L2 1e-5."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_bit_quantized_amd as m
+    m.lib()
+    from nvfp4_bit_quantized_amd import linear
+    return linear
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def _t(q):
+    """The transposed copy of a 2D-quantized weight as an oracle operand."""
+    return dict(codes=q["codes_t"], scales=q["scales_t"], layout=1, s_dec=q["s_dec"])
+
+
+@pytest.mark.parametrize("T,fin,fout", [(64, 128, 96), (256, 80, 48)])
+def test_linear_matches_oracle(L, orc, T, fin, fout):
+    x = W.act((T, fin), 11).float()
+    w = W.weight((fout, fin), 12).float()
+    dy = W.grad((T, fout), 13).float()
+    sign, sd, sw = 0x51E40004, 0x5EED0003, 0x5EED0004
+    xd = x.to(DEV).requires_grad_(True)
+    wd = w.to(DEV).requires_grad_(True)
+    y = L.NVFP4LinearFn.apply(xd, wd, sign, sd, sw)
+    y.backward(dy.to(DEV))
+    xb, wb, dyb = W.bits(x), W.bits(w), W.bits(dy)
+    ox, ow = orc.quantize_1d(xb), orc.quantize_2d(wb)
+    ody = orc.quantize_1d(dyb, rounding=1, seed=sd)
+    oxt = orc.hadamard_quantize(xb, sign, 0, 0)
+    odyt = orc.hadamard_quantize(dyb, sign, 1, sw)
+    y_ref = orc.gemm_f64(ox, ow, T, fout, fin)
+    dx_ref = orc.gemm_f64(ody, _t(ow), T, fin, fout)
+    dw_ref = orc.gemm_f64(odyt, oxt, fout, fin, T)
+    assert _rel(y.detach().cpu().numpy(), y_ref) <= 1e-5
+    assert _rel(xd.grad.cpu().numpy(), dx_ref) <= 1e-5
+    assert _rel(wd.grad.cpu().numpy(), dw_ref) <= 1e-5
+
+
+def test_high_precision_flag_is_torch_linear(L):
+    torch.manual_seed(0)
+    m = L.NVFP4Linear(128, 64, high_precision=True)
+    with torch.no_grad():
+        m.weight.copy_(W.weight((64, 128), 3).to(DEV))
+    x = W.act((32, 128), 4).to(DEV).requires_grad_(True)
+    y = m(x)
+    y_ref = torch.nn.functional.linear(x, m.weight)
+    assert torch.equal(y, y_ref)
+
+
+def test_reproducible_and_seeded(L):
+    x = W.act((64, 128), 21).to(DEV)
+    dy = W.grad((64, 96), 22).to(DEV)
+    grads = []
+    for seed in (5, 5, 6):
+        m = L.NVFP4Linear(128, 96, seed=seed)
+        with torch.no_grad():
+            m.weight.copy_(W.weight((96, 128), 23).to(DEV))
+        xi = x.clone().requires_grad_(True)
+        m(xi).backward(dy)
+        grads.append((xi.grad.clone(), m.weight.grad.clone()))
+    assert torch.equal(grads[0][0], grads[1][0]) and torch.equal(grads[0][1], grads[1][1])
+    assert not torch.equal(grads[0][0], grads[2][0])
+
+
+def _ffn(L, d, ff, hp, w1, w2, seed):
+    up = L.NVFP4Linear(d, ff, high_precision=hp, seed=seed)
+    down = L.NVFP4Linear(ff, d, high_precision=hp, seed=seed + 1)
+    with torch.no_grad():
+        up.weight.copy_(w1)
+        down.weight.copy_(w2)
+    return up, down
+
+
+def _ffn_step(up, down, x, dy):
+    xi = x.clone().requires_grad_(True)
+    y = down(torch.nn.functional.gelu(up(xi)))
+    y.backward(dy)
+    return y.detach().float(), xi.grad.float(), up.weight.grad.float(), down.weight.grad.float()
+
+
+def test_ffn_pair_against_bf16(L):
+    """The FFN linear pair (up 5120 -> 20480, GELU, down 20480 -> 5120) over 2048 tokens in
+    bf16: the NVFP4 layers' output and gradients differ from the BF16 pair's by the compounded
+    quantization error of their operands; with both layers flagged high-precision the pair is
+    exactly the BF16 pair.
+
+    Bound: the relative quantization error e of one operand is measured here with the noise
+    diagnostic (||Q(t) - t|| / ||t|| for x with RNE and dy with SR).  The forward output carries
+    the errors of four quantized operands (x, W1, the hidden activation, W2), each gradient those
+    of up to six; independent errors add in quadrature, so the output error stays below
+    2 e_max * 1.25 and the gradient errors below sqrt(6) e_max * 1.25 (25% margin)."""
+    import nvfp4_bit_quantized_amd as nvm
+    T, d, ff = 2048, W.CFG5["d_model"], W.CFG5["d_ff"]
+    x = W.act((T, d), 601).to(DEV)
+    w1 = W.weight((ff, d), 602).to(DEV)
+    w2 = W.weight((d, ff), 603).to(DEV)
+    dy = W.grad((T, d), 604).to(DEV)
+    e_x = 1.0 / nvm.noise_report(nvm.quantize_1d_noise(x, nvm.RNE)[1])["ratio"]
+    e_dy = 1.0 / nvm.noise_report(nvm.quantize_1d_noise(dy, nvm.SR, 7)[1])["ratio"]
+    e = max(e_x, e_dy)
+    ref = _ffn_step(*_ffn(L, d, ff, True, w1, w2, 1), x, dy)
+    up, down = _ffn(L, d, ff, False, w1, w2, 1)
+    got = _ffn_step(up, down, x, dy)
+    errs = [float(torch.linalg.norm(g - r) / torch.linalg.norm(r)) for g, r in zip(got, ref)]
+    print(f"operand errors x {e_x:.4f} dy {e_dy:.4f}; rel L2 vs bf16 (y, dx, dW1, dW2):",
+          [round(v, 4) for v in errs])
+    assert 0.0 < errs[0] < 2.0 * e * 1.25, (errs, e)
+    assert all(0.0 < v < 6 ** 0.5 * e * 1.25 for v in errs[1:]), (errs, e)
+    hp = _ffn_step(*_ffn(L, d, ff, True, w1, w2, 1), x, dy)
+    assert all(torch.equal(a, b) for a, b in zip(hp, ref))
