@@ -172,6 +172,25 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dtype dt, in
 nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                         int64_t ldc, void *stream);
 
+/* Format sweep [P2 Describir: block size, scale format and rounding method are the FP4 design
+ * choices explored, and 16-element blocks with E4M3 scales (NVFP4) come out best]: quantize
+ * x [rows x cols] (row stride ld) with `block` (8, 16 or 32) elements per scale along the row and
+ * the scale format `scale_fmt`
+ *   0: E4M3 block scale under the fp32 per-tensor scale (the NVFP4 steps),
+ *   1: E8M0 power-of-two scale 2^(floor(log2 amax_b) - 2), no tensor scale (the MXFP4 steps),
+ * round RNE or SR (element index row * cols + col), and write the dequantized fp32 values to y
+ * (row stride ldy, 16-byte aligned rows).  No codes are kept: this measures formats.  Block 16 /
+ * format 0 reproduces nvfp4_dequantize of nvfp4_quantize_1d; block 32 / format 1 that of
+ * mxfp4_quantize_1d.  amax_in (format 0 only): the tensor amax, or NULL to compute it into
+ * *amax_out, which is then required.  amax_out (optional): the amax used (0 for format 1).
+ * sums (optional, two doubles, overwritten): sum x^2 and sum (y - x)^2, accumulated in fp64 with
+ * device atomics (run-dependent order in the last bits).  Unknown block or format:
+ * NVFP4_ERR_SHAPE / NVFP4_ERR_DTYPE. */
+nvfp4_status nvfp4_qdq(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                       int32_t block, int32_t scale_fmt, const float *amax_in, nvfp4_round rnd,
+                       uint64_t seed, float *y, int64_t ldy, float *amax_out, double *sums,
+                       void *stream);
+
 /* MXFP4 quantization (the comparison format of [P3 NVFP4 in pratica]): 32-element blocks along
  * cols with an E8M0 scale 2^(floor(log2 amax_b) - 2) (byte = exponent + 127, clamped to
  * [0, 254]; an all-zero block gets byte 127); codes E2M1 of x * 2^-exponent, RNE or SR as above.

@@ -23,7 +23,7 @@ BLK_1x16, BLK_16x16, MX_1x32 = 0, 1, 2
 SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_quantize_1d",
            "nvfp4_quantize_2d", "nvfp4_hadamard_quantize", "nvfp4_dequantize", "nvfp4_gemm",
            "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual",
-           "nvfp4_quantize_1d_noise")
+           "nvfp4_quantize_1d_noise", "nvfp4_qdq")
 
 
 class NvTensor(C.Structure):
@@ -59,6 +59,7 @@ def lib():
         L.nvfp4_dual_amax.argtypes = [P, i32, i64, i64, i64, u64, P, P, P]
         L.nvfp4_quantize_dual.argtypes = [P, i32, i64, u64, P, P, i32, u64, u64, T, T, P]
         L.nvfp4_quantize_1d_noise.argtypes = [P, i32, i64, P, i32, u64, T, P, P]
+        L.nvfp4_qdq.argtypes = [P, i32, i64, i64, i64, i32, i32, P, i32, u64, P, i64, P, P, P]
         for name in SYMBOLS[1:]:
             getattr(L, name).restype = i32
         _lib = L
@@ -169,6 +170,23 @@ def quantize_1d_noise(x: torch.Tensor, rounding: int = SR, seed: int = 0,
            lib().nvfp4_quantize_1d_noise(_ptr(x), dt, ld, _ptr(amax_in), rounding, seed,
                                          C.byref(d), _ptr(sums), _stream(x.device)))
     return q, sums
+
+
+E4M3, E8M0 = 0, 1
+
+
+def qdq(x: torch.Tensor, block: int, scale_fmt: int, rounding: int = RNE, seed: int = 0,
+        amax_in: torch.Tensor | None = None, out: torch.Tensor | None = None,
+        sums: torch.Tensor | None = None, amax_out: torch.Tensor | None = None):
+    """Format sweep: x quantized with `block` (8/16/32) elements per scale in `scale_fmt` (E4M3
+    under the tensor scale, or E8M0) and dequantized -> (y fp32, amax used, sums)."""
+    x, dt, ld = _x(x)
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device) if out is None else out
+    amax_out = torch.empty(1, dtype=torch.float32, device=x.device) if amax_out is None else amax_out
+    _check("nvfp4_qdq", lib().nvfp4_qdq(_ptr(x), dt, x.shape[0], x.shape[1], ld, block, scale_fmt,
+                                        _ptr(amax_in), rounding, seed, _ptr(y), y.stride(0),
+                                        _ptr(amax_out), _ptr(sums), _stream(x.device)))
+    return y, amax_out, sums
 
 
 def noise_report(sums: torch.Tensor) -> dict:

@@ -415,6 +415,101 @@ k_mx_quant(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, ui
     }
 }
 
+// ---- format sweep: quantize-dequantize with a chosen block size and scale format -------------
+// [P2 Describir: block size, scale format and rounding are the FP4 design choices explored.]
+// One lane per block of B (8, 16 or 32) elements.  kE8M0 = false: E4M3 block scale under the
+// per-tensor fp32 scale (the NVFP4 steps); true: E8M0 scale 2^(floor(log2 amax_b) - 2), no
+// tensor scale (the MXFP4 steps).  Writes the dequantized fp32 values and, when sums is
+// non-NULL, adds sum x^2 and sum (y - x)^2 (fp64, one atomic pair per workgroup).
+template <typename T, int B, bool kE8M0, bool kSR>
+__global__ void __launch_bounds__(kThreads)
+k_qdq(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uint32_t cols,
+      const float* __restrict__ amax_src, uint64_t seed, float* __restrict__ y, int64_t ldy,
+      double* sums) {
+    const uint32_t b = blockIdx.x * kThreads + threadIdx.x;
+    TensorScales ts{448.0f, 1.0f, 1.0f};
+    if constexpr (!kE8M0) ts = tensor_scales(*amax_src);
+    double g2 = 0.0, e2 = 0.0;
+    if (b < blocks) {
+        const uint32_t row = fastdiv(b, bpr), cb = b - row * bpr.d;
+        const T* p = x + (int64_t)row * ld + cb * B;
+        float v[B];
+#pragma unroll
+        for (int g = 0; g < B / 8; ++g) Group8<T>::load(p + 8 * g, v + 8 * g);
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < B; ++e) m = fmaxf(m, fabsf(v[e]));
+        uint32_t sb = 0;
+        float enc = 0.0f;
+        int e8 = 0;
+        if constexpr (kE8M0) {
+            if (m > 0.0f) {
+                e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;
+                e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
+            }
+        } else {
+            block_scale(m, ts, sb, enc);
+        }
+        const float sc = kE8M0 ? 1.0f : e4m3_decode(sb);
+        float* out = y + (int64_t)row * ldy + cb * B;
+#pragma unroll
+        for (int g = 0; g < B / 8; ++g) {
+            float z[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ze = kE8M0 ? __builtin_amdgcn_ldexpf(v[8 * g + e], -e8) : v[8 * g + e] * enc;
+                z[e] = kSR ? ze + ze : ze;
+            }
+            uint32_t packed;
+            if constexpr (kSR) {
+                const u32x4 w = sr_words(seed, (uint64_t)row * cols + cb * B + 8 * g);
+                const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+                packed = e2m1_sr_pack8(z, words);
+            } else {
+                packed = e2m1_rne_pack8(z);
+            }
+            float q[8];
+            e2m1_decode8(packed, q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                q[e] = kE8M0 ? __builtin_amdgcn_ldexpf(q[e], e8) : (q[e] * sc) * ts.s_dec;
+            reinterpret_cast<float4*>(out + 8 * g)[0] = make_float4(q[0], q[1], q[2], q[3]);
+            reinterpret_cast<float4*>(out + 8 * g)[1] = make_float4(q[4], q[5], q[6], q[7]);
+            if (sums) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double xv = v[8 * g + e], d = (double)q[e] - xv;
+                    g2 += xv * xv;
+                    e2 += d * d;
+                }
+            }
+        }
+    }
+    if (sums) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            g2 += __shfl_xor(g2, off);
+            e2 += __shfl_xor(e2, off);
+        }
+        __shared__ double part[2][kThreads / 64];
+        if ((threadIdx.x & 63) == 0) {
+            part[0][threadIdx.x >> 6] = g2;
+            part[1][threadIdx.x >> 6] = e2;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double a = 0.0, c = 0.0;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w) {
+                a += part[0][w];
+                c += part[1][w];
+            }
+            atomicAdd(sums, a);
+            atomicAdd(sums + 1, c);
+        }
+    }
+}
+
 static int stream_grid(uint32_t groups, int unroll = kUnroll) {
     int64_t n = ((int64_t)groups + kThreads * unroll - 1) / (kThreads * unroll);
     return (int)(n < 1 ? 1 : n);
@@ -621,5 +716,53 @@ extern "C" nvfp4_status mxfp4_quantize_1d(const void* x, nvfp4_dtype dt, int64_t
         if (rnd == NVFP4_SR) NVFP4_MXQ(float, true); else NVFP4_MXQ(float, false);
     }
 #undef NVFP4_MXQ
+    return launch_status();
+}
+
+extern "C" nvfp4_status nvfp4_qdq(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                  int64_t ld, int32_t block, int32_t scale_fmt,
+                                  const float* amax_in, nvfp4_round rnd, uint64_t seed, float* y,
+                                  int64_t ldy, float* amax_out, double* sums, void* stream) {
+    nvfp4_status s = check_input(x, dt, rows, cols, ld);
+    if (s) return s;
+    if (block != 8 && block != 16 && block != 32) return NVFP4_ERR_SHAPE;
+    if (scale_fmt != 0 && scale_fmt != 1) return NVFP4_ERR_DTYPE;
+    if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
+    if (cols % block != 0 || too_big(rows, cols)) return NVFP4_ERR_SHAPE;
+    s = check_input(y, NVFP4_F32, rows, cols, ldy);
+    if (s) return s;
+    if (scale_fmt == 0 && !amax_in && !amax_out) return NVFP4_ERR_NULL;
+    if (amax_out && (reinterpret_cast<uintptr_t>(amax_out) & 3u)) return NVFP4_ERR_ALIGN;
+    if (sums && (reinterpret_cast<uintptr_t>(sums) & 7u)) return NVFP4_ERR_ALIGN;
+    hipStream_t st = as_stream(stream);
+    const float* src = amax_in;
+    if (scale_fmt == 0 && !src) {
+        s = launch_amax(x, dt, rows, cols, ld, amax_out, st);
+        if (s) return s;
+        src = amax_out;
+    } else if (amax_out) {
+        hipLaunchKernelGGL(k_tensor_scalars, dim3(1), dim3(1), 0, st,
+                           scale_fmt == 0 ? src : nullptr, amax_out, nullptr);
+    }
+    if (sums) hipLaunchKernelGGL(k_fill_f64x2, dim3(1), dim3(1), 0, st, sums);
+    const uint32_t blocks = (uint32_t)(rows * (cols / block));
+    if (blocks == 0) return launch_status();
+    const FastDiv bpr = make_fastdiv((uint32_t)(cols / block));
+    const dim3 grid((blocks + kThreads - 1) / kThreads), blk(kThreads);
+#define NVFP4_QDQ(TT, BB, E8, SRV)                                                                \
+    hipLaunchKernelGGL((k_qdq<TT, BB, E8, SRV>), grid, blk, 0, st, static_cast<const TT*>(x), ld, \
+                       blocks, bpr, (uint32_t)cols, src, seed, y, ldy, sums)
+#define NVFP4_QDQ_R(TT, BB, E8)                                                                   \
+    if (rnd == NVFP4_SR) NVFP4_QDQ(TT, BB, E8, true); else NVFP4_QDQ(TT, BB, E8, false)
+#define NVFP4_QDQ_F(TT, BB)                                                                       \
+    if (scale_fmt == 1) NVFP4_QDQ_R(TT, BB, true); else NVFP4_QDQ_R(TT, BB, false)
+#define NVFP4_QDQ_B(TT)                                                                           \
+    if (block == 8) NVFP4_QDQ_F(TT, 8); else if (block == 16) NVFP4_QDQ_F(TT, 16);               \
+    else NVFP4_QDQ_F(TT, 32)
+    if (dt == NVFP4_BF16) { NVFP4_QDQ_B(uint16_t); } else { NVFP4_QDQ_B(float); }
+#undef NVFP4_QDQ_B
+#undef NVFP4_QDQ_F
+#undef NVFP4_QDQ_R
+#undef NVFP4_QDQ
     return launch_status();
 }

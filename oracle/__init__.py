@@ -89,6 +89,8 @@ def lib():
         L.or_mx_dequantize.argtypes = [P, P, i64, i64, P, i64]
         L.or_mx_gemm_f64.restype = i32
         L.or_mx_gemm_f64.argtypes = [P, P, P, P, i64, i64, i64, P, i64, P]
+        L.or_qdq.restype = i32
+        L.or_qdq.argtypes = [P, i32, i64, i64, i64, i32, i32, P, i32, u64, P, P]
         L.or_e2m1_rne_n.restype = None
         L.or_e2m1_rne_n.argtypes = [P, i64, P]
         L.or_e2m1_sr_n.restype = None
@@ -298,6 +300,21 @@ def quant_noise(x: np.ndarray, q: dict) -> tuple[float, float]:
     rows, cols = xv.shape
     qv = dequantize(q, rows, cols).astype(np.float64)
     return float(np.sum(xv * xv)), float(np.sum((qv - xv) ** 2))
+
+
+def qdq(x: np.ndarray, block: int, scale_fmt: int, rounding: int = RNE, seed: int = 0,
+        amax_in: float | None = None):
+    """Format sweep: quantize with `block` elements per scale (8, 16, 32) and scale format
+    `scale_fmt` (0: E4M3 under the fp32 tensor scale; 1: E8M0 power of two), dequantize.
+    Returns (y float32 [rows x cols], tensor amax used (0 for E8M0))."""
+    x, dt = _input(x)
+    rows, cols = x.shape
+    y = np.zeros((rows, cols), dtype=np.float32)
+    am = np.zeros(1, dtype=np.float32)
+    ain = None if amax_in is None else np.array([amax_in], dtype=np.float32)
+    _check(lib().or_qdq(_ptr(x), dt, rows, cols, cols, int(block), int(scale_fmt), _ptr(ain),
+                        int(rounding), int(seed), _ptr(y), _ptr(am)), "qdq")
+    return y, float(am[0])
 
 
 def gemm_f64(a: dict, b: dict, M: int, N: int, K: int, rows: np.ndarray | None = None) -> np.ndarray:

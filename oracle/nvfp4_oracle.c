@@ -629,6 +629,75 @@ int or_mx_quantize_1d(const void *x, int dtype, int64_t rows, int64_t cols, int6
     return err ? OR_ERR_NONFINITE : OR_OK;
 }
 
+/* Format sweep ("FP4 All the Way", Describir: block size, scale format and rounding method are
+ * the FP4 design choices the authors explore).  Quantize x with `block` elements per scale along
+ * the row and the scale format `scale_fmt`, then dequantize into y [rows x cols] (fp32, dense):
+ *   scale_fmt 0: E4M3 block scale under the per-tensor fp32 scale, the NVFP4 steps of
+ *                or_quantize_1d with the block size as a parameter; y = (v * scale) * s_dec;
+ *   scale_fmt 1: E8M0 scale 2^(floor(log2 amax_b) - 2), no tensor scale, the steps of
+ *                or_mx_quantize_1d with the block size as a parameter; y = v * 2^e.
+ * Rounding RNE or SR (element index r * cols + k).  amax_out receives the tensor amax used
+ * (E4M3) or 0 (E8M0). */
+int or_qdq(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld, int block,
+           int scale_fmt, const float *amax_in, int rounding, uint64_t seed, float *y,
+           float *amax_out)
+{
+    if (block != 8 && block != 16 && block != 32) return OR_ERR_SHAPE;
+    if (scale_fmt != 0 && scale_fmt != 1) return OR_ERR_SHAPE;
+    if (cols % block != 0 || rows < 0 || cols < 0 || ld < cols) return OR_ERR_SHAPE;
+    float A = 0.0f, ts[3] = {1.0f, 1.0f, 1.0f};
+    if (scale_fmt == 0) {
+        if (amax_in) A = *amax_in;
+        else {
+            int rc = or_amax(x, dtype, rows, cols, ld, &A);
+            if (rc) return rc;
+        }
+        or_tensor_scales(A, ts);
+    }
+    int64_t nb = cols / block;
+    int err = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float v[32], ab = 0.0f;
+            for (int i = 0; i < block; ++i) {
+                v[i] = load_elem(x, dtype, r * ld + b * block + i);
+                if (!isfinite(v[i])) err = 1;
+                if (fabsf(v[i]) > ab) ab = fabsf(v[i]);
+            }
+            unsigned sb = 0;
+            float enc = 0.0f;
+            int e = 0;
+            if (scale_fmt == 0) {
+                block_scale(ab, ts, &sb, &enc);
+            } else if (ab > 0.0f) {
+                int E;
+                frexp((double)ab, &E);
+                e = (E - 1) - 2;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            for (int i = 0; i < block; ++i) {
+                int64_t k = b * block + i;
+                float z = scale_fmt == 0 ? v[i] * enc : ldexpf(v[i], -e);
+                unsigned code = (rounding == OR_SR)
+                    ? or_e2m1_sr(z, or_sr_bits(seed, (uint64_t)(r * cols + k)))
+                    : or_e2m1_rne(z);
+                float q = (float)or_e2m1_value(code);
+                if (scale_fmt == 0) {
+                    float sc = (float)or_e4m3_value(sb);
+                    float t = q * sc;
+                    y[r * cols + k] = t * ts[2];
+                } else {
+                    y[r * cols + k] = ldexpf(q, e);
+                }
+            }
+        }
+    if (err) return OR_ERR_NONFINITE;
+    if (amax_out) *amax_out = A;
+    return OR_OK;
+}
+
 int or_mx_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
                      float *out, int64_t ld)
 {

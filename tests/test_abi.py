@@ -135,3 +135,19 @@ def test_noise_validation(L):
     assert L.nvfp4_quantize_1d_noise(FAKE, nv.BF16, 16, None, nv.SR, 0, C.byref(q), FAKE,
                                      None) == nv.ERR_SHAPE
 
+
+def test_qdq_validation(L):
+    def call(block=16, fmt=0, rnd=nv.RNE, y=FAKE, ldy=64, amax_in=None, amax_out=FAKE, sums=None,
+             x=FAKE, cols=64):
+        return L.nvfp4_qdq(x, nv.BF16, 8, cols, 64, block, fmt, amax_in, rnd, 0, y, ldy, amax_out,
+                           sums, None)
+    assert call(block=12) == nv.ERR_SHAPE
+    assert call(fmt=2) == nv.ERR_DTYPE
+    assert call(rnd=3) == nv.ERR_DTYPE
+    assert call(cols=40, block=32) == nv.ERR_SHAPE
+    assert call(y=None) == nv.ERR_NULL
+    assert call(ldy=32) == nv.ERR_SHAPE
+    assert call(amax_out=None) == nv.ERR_NULL
+    assert call(sums=FAKE + 4) == nv.ERR_ALIGN
+    assert call(x=FAKE + 2) == nv.ERR_ALIGN
+
