@@ -58,8 +58,55 @@ __device__ __forceinline__ uint32_t rht_sign_mask(uint64_t sign_seed) {
     return philox4x32_10(0u, 0u, 0u, 0u, (uint32_t)sign_seed, (uint32_t)(sign_seed >> 32)).x & 0xFFFFu;
 }
 
-// In place: v <- H16 D v with butterflies in the order h = 1, 2, 4, 8 (no 1/4 factor).
-__device__ __forceinline__ void hd16(float* v, uint32_t sign_mask) {
+// For the amax only: |H16 D v| as a butterfly network on the unsigned input.  With v = c (.) u (c
+// a vector of signs carried per position, starting at c = d), a butterfly on (i, i + h) gives
+// c_i (u_i + s u_{i+h}) and c_i (u_i - s u_{i+h}) with s = c_i c_{i+h}: each butterfly is a pair of
+// fmas with a sign factor s, and the carried sign of position i + h becomes c_i.  Since s = +-1
+// the fma rounds exactly like the add or subtract and RNE commutes with negation, so |u_i| equals
+// |(H16 D v)_i| bit for bit (only the sign of an exact zero can differ, which the amax ignores).
+// The quantizer, whose codes keep the sign of zero, uses rht16 below.  The sign factors are the
+// same for every thread and kept as integer bit patterns so that they live in scalar registers.
+struct RhtPlan {
+    uint32_t s[32];     // +-1.0f bit patterns, stage by stage
+};
+
+__device__ __forceinline__ RhtPlan rht_plan(uint32_t sign_mask) {
+    RhtPlan p;
+    sign_mask = __builtin_amdgcn_readfirstlane(sign_mask);    // the same in every lane
+    uint32_t c[16];     // sign bit of c_i
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = ((sign_mask >> i) & 1u) << 31;
+    int k = 0;
+#pragma unroll
+    for (int hs = 1; hs < 16; hs <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if ((i & hs) == 0) {
+                p.s[k++] = 0x3F800000u | (c[i] ^ c[i + hs]);
+                c[i + hs] = c[i];
+            }
+    return p;
+}
+
+// In place: |v| <- |H16 D v| (signs and the 1/4 not applied).
+__device__ __forceinline__ void hd16_abs(float* v, const RhtPlan& p) {
+    int k = 0;
+#pragma unroll
+    for (int hs = 1; hs < 16; hs <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if ((i & hs) == 0) {
+                const float a = v[i], b = v[i + hs];
+                const float sk = __uint_as_float(p.s[k]);
+                v[i] = __builtin_fmaf(sk, b, a);
+                v[i + hs] = __builtin_fmaf(-sk, b, a);
+                ++k;
+            }
+}
+
+// In place: v <- (1/4) H16 D v with D applied first and butterflies in the order h = 1, 2, 4, 8.
+__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
+    sign_mask = __builtin_amdgcn_readfirstlane(sign_mask);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
 #pragma unroll
@@ -71,11 +118,6 @@ __device__ __forceinline__ void hd16(float* v, uint32_t sign_mask) {
                 v[i] = a + b;
                 v[i + hs] = a - b;
             }
-}
-
-// In place: v <- (1/4) H16 D v.
-__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
-    hd16(v, sign_mask);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
 }
@@ -105,40 +147,79 @@ __device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
 // publishing its maximum once (publish_amax).  The factor 1/4 of the transform is applied to the
 // maximum instead of to every element: scaling by 1/4 and fp32 rounding are both monotonic, so
 // fl(max|t| / 4) = max fl(|t| / 4).
-// A workgroup of kRhtAmaxSub x 256 threads works on kRhtAmaxSub tiles at a time.  With kPlain
-// the same pass also takes the amax of x itself (for the fused dual-orientation quantizer).
+// A workgroup of rht_amax_sub<T> x 256 threads works on that many tiles at a time.  Each thread
+// loads the next tile while it transforms the current one (bf16; fp32 tiles take twice the
+// registers and are not double-buffered).  Coordinates past the edges are clamped to the last
+// valid token chunk / feature group / tile: the duplicates they read leave a maximum unchanged, so
+// every load is unconditional.  With kPlain the same pass also takes the amax of x itself (for
+// the fused dual-orientation quantizer).
+// The amax tiles are wider than the quantizer's: 256 features x 8 chunks per 256 threads (a wave
+// reads 512 contiguous bytes of each of two token rows per load, instead of 128 bytes of eight),
+// which suits HBM better; the quantizer keeps 64-feature tiles for its feature-major stores.
 constexpr int kRhtAmaxBlocks = 256;
-constexpr int kRhtAmaxSub = 4;
+constexpr int kAmaxFeat = 256, kAmaxChunks = 8;
+template <typename T> constexpr int rht_amax_sub() { return 2; }
 
 template <typename T, bool kPlain>
+__device__ __forceinline__ void rht_amax_tile(const Tile16x8<T>& t16, const RhtPlan& plan, float& m,
+                                              float& mp) {
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = t16.get(i, f);
+        if constexpr (kPlain) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mp = fmaxf(mp, fabsf(v[i]));
+        }
+        hd16_abs(v, plan);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+}
+
+template <typename T, bool kPlain, int kRhtAmaxSub = rht_amax_sub<T>()>
 __global__ void __launch_bounds__(kRhtThreads * kRhtAmaxSub)
 k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
            float* amax_out, float* amax_plain_out, uint32_t tiles, FastDiv tiles_per_row) {
-    const uint32_t mask = rht_sign_mask(sign_seed);
+    const RhtPlan plan = rht_plan(rht_sign_mask(sign_seed));
     const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) % (kRhtThreads / 64);
     const uint32_t sub = threadIdx.x / kRhtThreads;
-    float m = 0.0f, mp = 0.0f;
-    for (uint32_t tile = blockIdx.x * kRhtAmaxSub + sub; tile < tiles;
-         tile += gridDim.x * kRhtAmaxSub) {
+    const int64_t last_c = Tn / 16 - 1, last_f0 = F - 8;
+    auto tile_ptr = [&](uint32_t tile) {
+        tile = tile < tiles ? tile : tiles - 1;
         const uint32_t ty = fastdiv(tile, tiles_per_row), tx = tile - ty * tiles_per_row.d;
-        const int64_t f0 = (int64_t)tx * kFeatPerBlock + (lane & 7) * 8;
-        const int64_t c = (int64_t)ty * kChunksPerBlock + wave * 8 + (lane >> 3);
-        if (f0 < F && c * 16 < Tn) {
-            Tile16x8<T> t16;
-            t16.load(x + c * 16 * ld + f0, ld);
-#pragma unroll
-            for (int f = 0; f < 8; ++f) {
-                float v[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = t16.get(i, f);
-                if constexpr (kPlain) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) mp = fmaxf(mp, fabsf(v[i]));
-                }
-                hd16(v, mask);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-            }
+        int64_t f0 = (int64_t)tx * kAmaxFeat + (lane & 31) * 8;
+        int64_t c = (int64_t)ty * kAmaxChunks + wave * 2 + (lane >> 5);
+        f0 = f0 < last_f0 ? f0 : last_f0;
+        c = c < last_c ? c : last_c;
+        return x + c * 16 * ld + f0;
+    };
+    float m = 0.0f, mp = 0.0f;
+    const uint32_t stride = gridDim.x * kRhtAmaxSub;
+    uint32_t tile = blockIdx.x * kRhtAmaxSub + sub;
+    if constexpr (sizeof(T) == 2) {
+        // two register sets with fixed roles; a clamped tile past the end is a harmless duplicate
+        Tile16x8<T> ta, tb;
+        float mb = 0.0f, mpb = 0.0f;
+        ta.load(tile_ptr(tile), ld);
+        for (; tile < tiles; tile += 2 * stride) {
+            tb.load(tile_ptr(tile + stride), ld);
+            __builtin_amdgcn_sched_barrier(0);
+            rht_amax_tile<T, kPlain>(ta, plan, m, mp);
+            __builtin_amdgcn_sched_barrier(0);
+            ta.load(tile_ptr(tile + 2 * stride), ld);
+            __builtin_amdgcn_sched_barrier(0);
+            rht_amax_tile<T, kPlain>(tb, plan, mb, mpb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        m = fmaxf(m, mb);
+        mp = fmaxf(mp, mpb);
+    } else {
+        for (; tile < tiles; tile += stride) {
+            Tile16x8<T> cur;
+            cur.load(tile_ptr(tile), ld);
+            rht_amax_tile<T, kPlain>(cur, plan, m, mp);
         }
     }
 #pragma unroll
@@ -332,12 +413,13 @@ static nvfp4_status launch_rht_amax(const void* x, nvfp4_dtype dt, int64_t T, in
                                     hipStream_t st) {
     hipLaunchKernelGGL(k_fill2_rht, dim3(1), dim3(1), 0, st, dst, plain_dst);
     if (T > 0 && F > 0) {
-        const dim3 g = rht_grid(T, F);
-        const uint32_t tiles = g.x * g.y;
-        const FastDiv tpr = make_fastdiv(g.x);
-        const uint32_t need = (tiles + kRhtAmaxSub - 1) / kRhtAmaxSub;
+        const uint32_t tx = (uint32_t)((F + kAmaxFeat - 1) / kAmaxFeat);
+        const uint32_t tiles = tx * (uint32_t)((T / 16 + kAmaxChunks - 1) / kAmaxChunks);
+        const FastDiv tpr = make_fastdiv(tx);
+        const int sub = dt == NVFP4_BF16 ? rht_amax_sub<uint16_t>() : rht_amax_sub<float>();
+        const uint32_t need = (tiles + sub - 1) / sub;
         const dim3 grid(need < (uint32_t)kRhtAmaxBlocks ? need : (uint32_t)kRhtAmaxBlocks);
-        const dim3 block(kRhtThreads * kRhtAmaxSub);
+        const dim3 block(kRhtThreads * sub);
 #define NVFP4_RA(TT, PLAIN)                                                                       \
         hipLaunchKernelGGL((k_rht_amax<TT, PLAIN>), grid, block, 0, st, static_cast<const TT*>(x), \
                            T, F, ld, sign_seed, dst, plain_dst, tiles, tpr)

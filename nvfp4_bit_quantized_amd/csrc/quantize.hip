@@ -232,9 +232,12 @@ __global__ void k_fill_f64x2(double* p) {
 }
 
 // ---- 2D quantization of weights [P1 Metodologia: two-dimensional block scaling] ---------------
-// A wave covers 4 tiles of 16x16; lane (t = lane/16, r = lane%16) holds row r of tile t (16
-// elements).  The tile amax is a max over the 16 lanes of the tile.  The transposed copy is
-// built by staging the tile's codes in LDS, one byte per element.
+// A wave covers kQ2Groups groups of 4 tiles of 16x16; in each group lane (t = lane/16,
+// r = lane%16) holds row r of tile t (16 elements).  All of a lane's loads are issued before any
+// arithmetic.  One group per wave measured fastest (four: 20 us instead of 18 on 4096^2 bf16).  The tile amax is a max over the 16 lanes of the tile.  The transposed copy is
+// built by staging each tile's codes in LDS, one byte per element.
+constexpr int kQ2Groups = 1;
+
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols, uint32_t tiles,
@@ -242,7 +245,8 @@ k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols, uin
           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
           uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
           float* amax_out, float* sdec_out, float* amax_out_t, float* sdec_out_t) {
-    __shared__ uint32_t stage[kThreads / 64][4][16][5];    // [wave][tile][row][16 bytes + pad]
+    // [wave][group][tile][row][16 code bytes + 4 bytes of padding]
+    __shared__ uint32_t stage[kThreads / 64][kQ2Groups][4][16][5];
     const float A = *amax_src;
     const TensorScales ts = tensor_scales(A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -253,57 +257,71 @@ k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols, uin
     }
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int t = lane >> 4, r = lane & 15;
-    const uint32_t tile = (blockIdx.x * (kThreads / 64) + wv) * 4 + t;
-    const bool valid = tile < tiles;
-    uint32_t ti = 0, tj = 0;
-    float y[16];
-    if (valid) {
-        ti = fastdiv(tile, tiles_per_row);
-        tj = tile - ti * tiles_per_row.d;
-        const T* p = w + (int64_t)(ti * 16 + r) * ld + tj * 16;
-        Group8<T>::load(p, y);
-        Group8<T>::load(p + 8, y + 8);
-    } else {
+    float y[kQ2Groups][16];
+    uint32_t ti[kQ2Groups], tj[kQ2Groups];
+    bool valid[kQ2Groups];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) y[e] = 0.0f;
+    for (int g = 0; g < kQ2Groups; ++g) {
+        const uint32_t tile = ((blockIdx.x * (kThreads / 64) + wv) * kQ2Groups + g) * 4 + t;
+        valid[g] = tile < tiles;
+        ti[g] = 0; tj[g] = 0;
+        if (valid[g]) {
+            ti[g] = fastdiv(tile, tiles_per_row);
+            tj[g] = tile - ti[g] * tiles_per_row.d;
+            const T* p = w + (int64_t)(ti[g] * 16 + r) * ld + tj[g] * 16;
+            Group8<T>::load(p, y[g]);
+            Group8<T>::load(p + 8, y[g] + 8);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) y[g][e] = 0.0f;
+        }
     }
-    float m = 0.0f;
+    uint32_t sbs[kQ2Groups];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(y[e]));
+    for (int g = 0; g < kQ2Groups; ++g) {
+        float m = 0.0f;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-    uint32_t sb;
-    float enc;
-    block_scale(m, ts, sb, enc);
-    float z[16];
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(y[g][e]));
 #pragma unroll
-    for (int e = 0; e < 16; ++e) z[e] = y[e] * enc;
-    const uint32_t lo = e2m1_rne_pack8(z), hi = e2m1_rne_pack8(z + 8);
-    // one code per byte for the transposed copy
+        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        uint32_t sb;
+        float enc;
+        block_scale(m, ts, sb, enc);
+        sbs[g] = sb;
+        float z[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t w = q < 2 ? lo : hi, sh = 16 * (q & 1);
-        const uint32_t n = (w >> sh) & 0xFFFFu;                 // codes 4q .. 4q+3
-        stage[wv][t][r][q] = (n & 0xFu) | ((n & 0xF0u) << 4) | ((n & 0xF00u) << 8) | ((n & 0xF000u) << 12);
+        for (int e = 0; e < 16; ++e) z[e] = y[g][e] * enc;
+        const uint32_t lo = e2m1_rne_pack8(z), hi = e2m1_rne_pack8(z + 8);
+        // one code per byte for the transposed copy
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t wd = q < 2 ? lo : hi, sh = 16 * (q & 1);
+            const uint32_t n = (wd >> sh) & 0xFFFFu;             // codes 4q .. 4q+3
+            stage[wv][g][t][r][q] = (n & 0xFu) | ((n & 0xF0u) << 4) | ((n & 0xF00u) << 8) |
+                                    ((n & 0xF000u) << 12);
+        }
+        if (valid[g]) {
+            *reinterpret_cast<uint2*>(codes + (int64_t)(ti[g] * 16 + r) * (cols / 2) + tj[g] * 8) =
+                make_uint2(lo, hi);
+            if (r == 0) scales[(int64_t)ti[g] * tiles_per_row.d + tj[g]] = (uint8_t)sb;
+        }
     }
-    if (valid) {
-        *reinterpret_cast<uint2*>(codes + (int64_t)(ti * 16 + r) * (cols / 2) + tj * 8) =
-            make_uint2(lo, hi);
-        if (r == 0) scales[(int64_t)ti * tiles_per_row.d + tj] = (uint8_t)sb;
-    }
+    if (!codes_t) return;
     __syncthreads();
-    if (valid && codes_t) {
+#pragma unroll
+    for (int g = 0; g < kQ2Groups; ++g) {
+        if (!valid[g]) continue;
         // column r of the tile becomes row (16 tj + r) of the transposed matrix
-        const uint8_t* st = reinterpret_cast<const uint8_t*>(&stage[wv][t][0][0]);
+        const uint8_t* st = reinterpret_cast<const uint8_t*>(&stage[wv][g][t][0][0]);
         uint32_t tlo = 0, thi = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             tlo |= (uint32_t)st[e * 20 + r] << (4 * e);
             thi |= (uint32_t)st[(e + 8) * 20 + r] << (4 * e);
         }
-        *reinterpret_cast<uint2*>(codes_t + (int64_t)(tj * 16 + r) * (rows / 2) + ti * 8) =
+        *reinterpret_cast<uint2*>(codes_t + (int64_t)(tj[g] * 16 + r) * (rows / 2) + ti[g] * 8) =
             make_uint2(tlo, thi);
-        if (r == 0) scales_t[(int64_t)tj * (rows / 16) + ti] = (uint8_t)sb;
+        if (r == 0) scales_t[(int64_t)tj[g] * (rows / 16) + ti[g]] = (uint8_t)sbs[g];
     }
 }
 
@@ -651,7 +669,7 @@ extern "C" nvfp4_status nvfp4_quantize_2d(const void* w, nvfp4_dtype dt, int64_t
         return launch_status();
     }
     const FastDiv tpr = make_fastdiv((uint32_t)(out->cols / 16));
-    const int tiles_per_block = (kThreads / 64) * 4;
+    const int tiles_per_block = (kThreads / 64) * 4 * kQ2Groups;
     const dim3 grid((tiles + tiles_per_block - 1) / tiles_per_block), block(kThreads);
     uint8_t* ct = out_t ? out_t->codes : nullptr;
     uint8_t* sct = out_t ? out_t->scales : nullptr;
