@@ -79,22 +79,22 @@ __device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts
 // Stochastic rounding of one element [P2 Describir: stochastic rounding in the backward pass]:
 // with lo <= |z| < hi the neighbouring grid values, round up iff r16 < 65536 (|z|-lo)/(hi-lo);
 // |z| >= 6 saturates; sign kept.  Works on z2 = 2z (callers form it as z + z, exact) whose grid
-// 0,1,2,3,4,6,8,12 has spacing 1 below 4, 2 in [4,8) and 4 above: scaling a2 = |z2| by
-// s = 1, 1/2 or 1/4 puts every region on an integer grid, so (|z|-lo)/(hi-lo) = fract(a2 s)
-// and the rounded value is floor(a2 s) + up, all exact in fp32.  The magnitude code is that
-// integer plus the region's offset (0, 2, 4), clamped to 7 (which also saturates a2 >= 12).
+// 0,1,2,3,4,6,8,12 has spacing 1 below 4, 2 in [4,8) and 4 above: scaling a2 = |z2| by 2^-k with
+// k = 0, 1, 2 for those regions (k + 2 = the binary exponent of a2 clamped to [2, 4]) puts every
+// region on an integer grid, so (|z|-lo)/(hi-lo) = fract(a2 2^-k) and the rounded value is
+// floor(a2 2^-k) + up, all exact in fp32.  The magnitude code is that integer plus 2k, clamped
+// to 7 (which also saturates a2 >= 12).
 __device__ __forceinline__ uint32_t e2m1_sr_code2(float z2, uint32_t r16) {
     const uint32_t zb = __float_as_uint(z2);
-    const uint32_t sign = (zb >> 28) & 8u;
-    const float a = __uint_as_float(zb & 0x7FFFFFFFu);
-    const uint32_t c4 = a >= 4.0f, c8 = a >= 8.0f;
-    const float s = c8 ? 0.25f : (c4 ? 0.5f : 1.0f);
-    const float as = a * s;
-    const float fl = __builtin_floorf(as);
-    const float f = as - fl;
+    const float a = __builtin_fabsf(z2);
+    const int e = __builtin_amdgcn_frexp_expf(a);            // a = m 2^e, m in [0.5, 1)
+    const int k2 = e < 2 ? 2 : (e > 4 ? 4 : e);              // k + 2
+    const float as = __builtin_amdgcn_ldexpf(a, 2 - k2);
+    const uint32_t fl = (uint32_t)as;                        // floor: as >= 0
+    const float f = __builtin_amdgcn_fractf(as);
     const uint32_t up = (float)r16 < f * 65536.0f;
-    const uint32_t idx = (uint32_t)fl + up + 2u * (c4 + c8);
-    return sign | (idx < 7u ? idx : 7u);
+    const uint32_t idx = fl + up + 2u * (uint32_t)(k2 - 2);
+    return ((zb >> 28) & 8u) | (idx < 7u ? idx : 7u);
 }
 
 // Eight codes: element e takes the 16-bit half (e & 1) of w[e >> 1] (low half first), packed
