@@ -44,6 +44,26 @@ struct MxStage {
     uint4 c[kPerThread];
     uint32_t s;
 
+    // K % 128 == 0: rows past the edge clamped to the last row (their results are never stored),
+    // k0 past the end clamped to the last step by the caller, so no load is conditional and the
+    // compiler's wait counts stay exact.
+    __device__ __forceinline__ void load_fast(const uint8_t* codes, const uint8_t* scales,
+                                              int64_t rows, int64_t row0, int k0, int K, int tid) {
+        static_assert(kChunks % NT == 0 && ROWS <= NT, "fast loader shape");
+        const int64_t rb = K / 2, nkb = K / 32;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int ch = tid + i * NT;
+            const int r = ch >> 2, q = ch & 3;
+            int64_t row = row0 + r;
+            row = row < rows - 1 ? row : rows - 1;
+            c[i] = *reinterpret_cast<const uint4*>(codes + row * rb + k0 / 2 + q * 16);
+        }
+        int64_t row = row0 + (tid < ROWS ? tid : 0);
+        row = row < rows - 1 ? row : rows - 1;
+        s = *reinterpret_cast<const uint32_t*>(scales + row * nkb + k0 / 32);
+    }
+
     __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                          int64_t row0, int k0, int K, int tid) {
         const int64_t rb = K / 2, nkb = K / 32;
@@ -84,7 +104,7 @@ struct MxStage {
     }
 };
 
-template <int WM, int WN, int TM, int TN, bool kBF16Out>
+template <int WM, int WN, int TM, int TN, bool kBF16Out, bool kFast>
 __global__ void __launch_bounds__(WM * WN * 64)
 k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
              const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
@@ -113,8 +133,13 @@ k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_
     MxStage<BM, NT> sa;
     MxStage<BN, NT> sb;
     const int nk = (K + kMxBK - 1) / kMxBK;
-    sa.load(a_codes, a_scales, M, m0, 0, K, tid);
-    sb.load(b_codes, b_scales, N, n0, 0, K, tid);
+    if constexpr (kFast) {
+        sa.load_fast(a_codes, a_scales, M, m0, 0, K, tid);
+        sb.load_fast(b_codes, b_scales, N, n0, 0, K, tid);
+    } else {
+        sa.load(a_codes, a_scales, M, m0, 0, K, tid);
+        sb.load(b_codes, b_scales, N, n0, 0, K, tid);
+    }
     sa.store(lds_a[0], lds_sa[0], tid);
     sb.store(lds_b[0], lds_sb[0], tid);
     __syncthreads();
@@ -122,7 +147,11 @@ k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_
     const int lrow = lane & 31, h = lane >> 5;
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) {
+        if constexpr (kFast) {
+            const int kn = (kt + 1 < nk ? kt + 1 : kt) * kMxBK;
+            sa.load_fast(a_codes, a_scales, M, m0, kn, K, tid);
+            sb.load_fast(b_codes, b_scales, N, n0, kn, K, tid);
+        } else if (kt + 1 < nk) {
             sa.load(a_codes, a_scales, M, m0, (kt + 1) * kMxBK, K, tid);
             sb.load(b_codes, b_scales, N, n0, (kt + 1) * kMxBK, K, tid);
         }
@@ -152,11 +181,18 @@ k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         va[i], vb[j], acc[i][j], kFmtFp4, kFmtFp4, 0, (int)ea[i], 0, (int)eb[j]);
         }
-        if (kt + 1 < nk) {
+        if (kFast || kt + 1 < nk) {
             sa.store(lds_a[cur ^ 1], lds_sa[cur ^ 1], tid);
             sb.store(lds_b[cur ^ 1], lds_sb[cur ^ 1], tid);
         }
-        __syncthreads();
+        if constexpr (kFast) {
+            // orders LDS only: the loads were all consumed by the stores above
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        } else {
+            __syncthreads();
+        }
     }
 
 #pragma unroll
@@ -200,11 +236,15 @@ extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     const uint32_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     const dim3 grid(nbm * nbn), block(WM * WN * 64);
     hipStream_t st = as_stream(stream);
-    if (c_dt == NVFP4_BF16)
-        hipLaunchKernelGGL((k_gemm_mxfp4<WM, WN, TM, TN, true>), grid, block, 0, st, a->codes, a->scales,
-                           b->codes, b->scales, (int)M, (int)N, (int)K, c, ldc);
-    else
-        hipLaunchKernelGGL((k_gemm_mxfp4<WM, WN, TM, TN, false>), grid, block, 0, st, a->codes,
-                           a->scales, b->codes, b->scales, (int)M, (int)N, (int)K, c, ldc);
+    const bool fast = K % kMxBK == 0;
+#define NVFP4_MX(BF, FAST)                                                                        \
+    hipLaunchKernelGGL((k_gemm_mxfp4<WM, WN, TM, TN, BF, FAST>), grid, block, 0, st, a->codes,     \
+                       a->scales, b->codes, b->scales, (int)M, (int)N, (int)K, c, ldc)
+    if (c_dt == NVFP4_BF16) {
+        if (fast) NVFP4_MX(true, true); else NVFP4_MX(true, false);
+    } else {
+        if (fast) NVFP4_MX(false, true); else NVFP4_MX(false, false);
+    }
+#undef NVFP4_MX
     return launch_status();
 }

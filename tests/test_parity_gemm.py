@@ -120,7 +120,8 @@ def test_gemm_wgrad_full(nv, orc):
     _check_gemm(nv, orc, qdy, qx, rows=_rows(4096, 128, seed=2), bf16_too=False)
 
 
-@pytest.mark.parametrize("M,N,K", [(32, 32, 64), (256, 256, 256), (100, 70, 96), (300, 520, 1056)])
+@pytest.mark.parametrize("M,N,K", [(32, 32, 64), (256, 256, 256), (100, 70, 96), (300, 520, 1056),
+                                   (300, 520, 1024), (512, 768, 2048)])
 def test_mx_gemm(nv, orc, M, N, K):
     a = W.act((M, K), 51)
     b = W.act((N, K), 52)
