@@ -379,6 +379,7 @@ extern "C" nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     if (s) return s;
     const int64_t M = a->rows, N = b->rows, K = a->cols;
     if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return NVFP4_ERR_SHAPE;
+    if (((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile) >= (1ll << 31)) return NVFP4_ERR_SHAPE;
     if (M == 0 || N == 0) return NVFP4_OK;
     const OperandDesc da{a->codes, a->scales, M, 0};
     const OperandDesc db{b->codes, b->scales, N, b->layout == NVFP4_BLK_16x16 ? 1 : 0};

@@ -230,6 +230,7 @@ extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     if (s) return s;
     const int64_t M = a->rows, N = b->rows, K = a->cols;
     if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return NVFP4_ERR_SHAPE;
+    if (((M + 255) / 256) * ((N + 255) / 256) >= (1ll << 31)) return NVFP4_ERR_SHAPE;   // grid
     if (M == 0 || N == 0) return NVFP4_OK;
     constexpr int WM = 2, WN = 2, TM = 4, TN = 4;
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;

@@ -397,7 +397,11 @@ static nvfp4_status check_rht_input(const void* x, nvfp4_dtype dt, int64_t T, in
     nvfp4_status s = check_input(x, dt, T, F, ld);
     if (s) return s;
     if (T % 16 != 0 || F % 8 != 0) return NVFP4_ERR_SHAPE;
-    if (T / 16 >= (1ll << 31) / kChunksPerBlock || F >= (1ll << 40)) return NVFP4_ERR_SHAPE;
+    // launch limits: quantizer grid (F/64, T/512) with gridDim.y <= 65535, and the amax pass's
+    // tile count (F/256 x T/128) in 31 bits
+    const int64_t gy = (T / 16 + kChunksPerBlock - 1) / kChunksPerBlock;
+    const int64_t amax_tiles = ((F + kAmaxFeat - 1) / kAmaxFeat) * ((T / 16 + kAmaxChunks - 1) / kAmaxChunks);
+    if (F >= (1ll << 31) || gy > 65535 || amax_tiles >= (1ll << 31)) return NVFP4_ERR_SHAPE;
     return NVFP4_OK;
 }
 

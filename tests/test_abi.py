@@ -151,3 +151,16 @@ def test_qdq_validation(L):
     assert call(sums=FAKE + 4) == nv.ERR_ALIGN
     assert call(x=FAKE + 2) == nv.ERR_ALIGN
 
+
+def test_launch_limits_are_rejected(L):
+    # shapes whose grids would not fit the launch limits fail validation (nothing is launched)
+    big = (1 << 31) - 256
+    a, b = _q(big, 64), _q(big, 64)
+    assert L.nvfp4_gemm(C.byref(a), C.byref(b), FAKE, nv.F32, big, None) == nv.ERR_SHAPE
+    ma, mb = _q(big, 64, layout=nv.MX_1x32), _q(big, 64, layout=nv.MX_1x32)
+    assert L.mxfp4_gemm(C.byref(ma), C.byref(mb), FAKE, nv.F32, big, None) == nv.ERR_SHAPE
+    T = 512 * 65536                                            # 65536 token blocks of 512
+    assert L.nvfp4_hadamard_amax(FAKE, nv.BF16, T, 16, 16, 1, FAKE, None) == nv.ERR_SHAPE
+    h = _q(16, T)
+    assert L.nvfp4_hadamard_quantize(FAKE, nv.BF16, 16, 1, None, nv.RNE, 0, C.byref(h), None) == nv.ERR_SHAPE
+
