@@ -151,8 +151,11 @@ nvfp4_status nvfp4_dual_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F
  *   out_t [F x T], layout 1x16: the Hadamard-transformed transposed copy (wgrad operand),
  *         bit-identical to nvfp4_hadamard_quantize(x, dt, ld, sign_seed, amax_t_in, rnd, seed_t,
  *         out_t).
- * amax_in / amax_t_in: the amax of x and of its transform; if either is NULL both are computed
- * first in one fused pass (nvfp4_dual_amax into out->amax and out_t->amax).  Requirements:
+ * amax_in / amax_t_in: the amax of x and of its transform, or NULL to compute that one first
+ * (both NULL: one fused pass as nvfp4_dual_amax into out->amax and out_t->amax; only amax_t_in
+ * NULL: the transform's amax into out_t->amax; only amax_in NULL: nvfp4_amax into out->amax).
+ * A supplied amax is never overwritten before it is used, even when it is out's own slot.
+ * Requirements:
  * T % 16 == 0, F % 16 == 0; out and out_t have distinct amax and s_dec pointers. */
 nvfp4_status nvfp4_quantize_dual(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
                                  const float *amax_in, const float *amax_t_in, nvfp4_round rnd,

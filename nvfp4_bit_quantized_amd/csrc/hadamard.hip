@@ -521,11 +521,16 @@ extern "C" nvfp4_status nvfp4_quantize_dual(const void* x, nvfp4_dtype dt, int64
     hipStream_t st = as_stream(stream);
     const float* src = amax_in;
     const float* src_t = amax_t_in;
-    if (!src || !src_t) {
-        s = launch_rht_amax(x, dt, T, F, ld, sign_seed, out_t->amax, out->amax, st);
+    // compute only the maxima the caller did not supply, so a supplied one is never overwritten
+    if (!src_t) {
+        s = launch_rht_amax(x, dt, T, F, ld, sign_seed, out_t->amax, src ? nullptr : out->amax, st);
         if (s) return s;
+        src_t = out_t->amax;
         if (!src) src = out->amax;
-        if (!src_t) src_t = out_t->amax;
+    } else if (!src) {
+        s = nvfp4_amax(x, dt, T, F, ld, out->amax, stream);
+        if (s) return s;
+        src = out->amax;
     }
     if (T == 0 || F == 0) {
         hipLaunchKernelGGL(k_scalars_rht, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);

@@ -70,6 +70,15 @@ def test_dual_strided_and_supplied_amax(nv, orc):
     _same_q(q, orc.quantize_1d(xb, amax_in=3.5), "amax_in rows")
     _same_q(qt, orc.hadamard_quantize(xb, SIGN, 0, 0), "amax_in transposed")
     at = torch.tensor([0.75], dtype=torch.float32, device=DEV)
+    q, qt = nv.quantize_dual(dv, SIGN, 0, amax_t_in=at)        # row-wise amax computed
+    _same_q(q, orc.quantize_1d(xb), "amax_t_in rows")
+    _same_q(qt, orc.hadamard_quantize(xb, SIGN, 0, 0, amax_in=0.75), "amax_t_in transposed")
+    # a supplied amax that lives in the output's own amax slot is used, not recomputed
+    qo = nv.QTensor.empty(64, 128, device=DEV)
+    qo.amax.fill_(3.5)
+    q, qt = nv.quantize_dual(dv, SIGN, 0, amax_in=qo.amax, out=qo)
+    _same_q(q, orc.quantize_1d(xb, amax_in=3.5), "aliased amax_in rows")
+    _same_q(qt, orc.hadamard_quantize(xb, SIGN, 0, 0), "aliased amax_in transposed")
     q, qt = nv.quantize_dual(dv, SIGN, 0, amax_in=a, amax_t_in=at)
     _same_q(q, orc.quantize_1d(xb, amax_in=3.5), "both given rows")
     _same_q(qt, orc.hadamard_quantize(xb, SIGN, 0, 0, amax_in=0.75), "both given transposed")
