@@ -27,6 +27,8 @@
 // K is permuted inside a step identically for both operands: MFMA k-slot (8h + j) of sub-step
 // s reads element 32h + 8s + j of the 64-element step, so a lane's 16 bytes cover two whole
 // NVFP4 blocks and one scale serves each sub-step.
+// Epilogue: bf16 results are staged per wave in the idle step buffers and leave as 128-byte
+// row pieces, 16 bytes per lane; fp32 results are stored directly, one column per lane.
 
 #include "device_codecs.hpp"
 #include "host_util.hpp"
@@ -215,13 +217,20 @@ __device__ __forceinline__ void read_frags(const LdsStepU& st, Frags<TM, TN>& f,
     }
 }
 
-template <int TM, int TN>
+// Accumulator layouts (the operand order does not change the sums or their speed):
+//   kT = false: element r of lane l is C[row 8*(r/4) + 4*(l/32) + r%4][col l%32] of the 32x32
+//               tile -- one column per lane;
+//   kT = true:  B is the MFMA's first operand and the tile is held transposed, element r of
+//               lane l is C[row l%32][col 8*(r/4) + 4*(l/32) + r%4] -- four consecutive columns
+//               of one row per r/4.
+template <int TM, int TN, bool kT>
 __device__ __forceinline__ void mfma_frags(const Frags<TM, TN>& f, float16v (&acc)[TM][TN]) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = kT ? __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // Quarter q of the next step: unpack dword q (8 codes, half an NVFP4 block) of this thread's A
@@ -242,28 +251,94 @@ __device__ __forceinline__ void store_quarter(LdsStepU& nxt, const FetchU& f, ha
 // step).  On exit f1 is loading this step's sub-step-3 fragments, left for the caller to
 // multiply after the barrier.  With do_store, the fetched codes `f` of the next step are
 // unpacked into `nxt` a quarter at a time between the MFMA groups.
-template <int TM, int TN>
+template <int TM, int TN, bool kT>
 __device__ __forceinline__ void step_pipe(const LdsStepU& cur, LdsStepU& nxt, const FetchU& f,
                                           bool do_store, float16v (&acc)[TM][TN],
                                           Frags<TM, TN>& f0, Frags<TM, TN>& f1, int wm, int wn,
                                           int lane, int tid) {
     const half2v sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.sa, 1.0f, false);
     const half2v sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.sb, 1.0f, false);
-    mfma_frags<TM, TN>(f1, acc);                       // previous step, sub-step 3
+    mfma_frags<TM, TN, kT>(f1, acc);                   // previous step, sub-step 3
     if (do_store) store_quarter(nxt, f, sa, sb, tid, 0);
     __builtin_amdgcn_sched_barrier(0);
     read_frags<TM, TN>(cur, f1, wm, wn, lane, 1);
-    mfma_frags<TM, TN>(f0, acc);                       // sub-step 0
+    mfma_frags<TM, TN, kT>(f0, acc);                   // sub-step 0
     if (do_store) store_quarter(nxt, f, sa, sb, tid, 1);
     __builtin_amdgcn_sched_barrier(0);
     read_frags<TM, TN>(cur, f0, wm, wn, lane, 2);
-    mfma_frags<TM, TN>(f1, acc);                       // sub-step 1
+    mfma_frags<TM, TN, kT>(f1, acc);                   // sub-step 1
     if (do_store) store_quarter(nxt, f, sa, sb, tid, 2);
     __builtin_amdgcn_sched_barrier(0);
     read_frags<TM, TN>(cur, f1, wm, wn, lane, 3);
-    mfma_frags<TM, TN>(f0, acc);                       // sub-step 2
+    mfma_frags<TM, TN, kT>(f0, acc);                   // sub-step 2
     if (do_store) store_quarter(nxt, f, sa, sb, tid, 3);
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---- epilogue --------------------------------------------------------------------------------
+// bf16 output, transposed layout (kT): each wave stages its 128 x 64 sub-tile of C (times alpha,
+// as bf16, 8 bytes per lane and r/4) in a private 16 KiB LDS region, then writes whole rows with
+// 16 bytes per lane, 8 rows of 128 bytes per store instruction (instead of 2 rows of 64 bytes
+// with 2 bytes per lane).  In the region a row's 16-byte chunks are permuted by (row / 2) % 8
+// so that neither the staging writes nor the row reads conflict on LDS banks.  vec: C and its
+// row stride are 16-byte aligned, else the staged values are stored one element at a time.
+template <int TM, int TN>
+__device__ __forceinline__ void epilogue_bf16(const float16v (&acc)[TM][TN], float alpha,
+                                              uint8_t* reg, int lane, int64_t r0, int64_t c0,
+                                              int M, int N, uint16_t* C, int64_t ldc, bool vec) {
+    static_assert(TM * 32 == 128 && TN * 32 == 64, "wave sub-tile");
+    const int lrow = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int row = i * 32 + lrow, c = 4 * j + g, p = c ^ ((row >> 1) & 7);
+                const float a0 = acc[i][j][4 * g] * alpha, a1 = acc[i][j][4 * g + 1] * alpha;
+                const float a2 = acc[i][j][4 * g + 2] * alpha, a3 = acc[i][j][4 * g + 3] * alpha;
+                *reinterpret_cast<uint2*>(reg + row * 128 + p * 16 + h * 8) =
+                    make_uint2(f32_to_bf16(a0) | (f32_to_bf16(a1) << 16),
+                               f32_to_bf16(a2) | (f32_to_bf16(a3) << 16));
+            }
+    __syncthreads();
+#pragma unroll 4
+    for (int pass = 0; pass < 16; ++pass) {
+        const int row = pass * 8 + (lane >> 3), c = lane & 7, p = c ^ ((row >> 1) & 7);
+        const uint4 v = *reinterpret_cast<const uint4*>(reg + row * 128 + p * 16);
+        const int64_t gr = r0 + row, gc = c0 + c * 8;
+        if (gr >= M || gc >= N) continue;
+        uint16_t* dst = C + gr * ldc + gc;
+        if (vec && gc + 8 <= N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (gc + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+// fp32 output, column-per-lane layout: for each r the 64 lanes store two rows of 32
+// consecutive floats (128 bytes each), which measured faster than staging 32 KiB per wave.
+template <int TM, int TN>
+__device__ __forceinline__ void epilogue_f32(const float16v (&acc)[TM][TN], float alpha, int lane,
+                                             int64_t r0, int64_t c0, int M, int N, float* C,
+                                             int64_t ldc) {
+    const int lrow = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = c0 + j * 32 + lrow;
+            if (col >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = r0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < M) C[row * ldc + col] = acc[i][j][r] * alpha;
+            }
+        }
 }
 
 // Waves are arranged WM x WN over the 256 x 256 tile, each owning TM x TN MFMA tiles of 32x32.
@@ -272,6 +347,8 @@ __global__ void __launch_bounds__(kThreads)
 k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __restrict__ sdA,
              const float* __restrict__ sdB, void* __restrict__ C, int64_t ldc) {
     static_assert(WM * WN == kThreads / 64 && WM * TM * 32 == kTile && WN * TN * 32 == kTile, "tile");
+    static_assert(sizeof(LdsStepU) * 2 >= (kThreads / 64) * 16384, "epilogue staging");
+    constexpr bool kT = kBF16Out;          // accumulator layout suited to each epilogue
     __shared__ LdsStepU st[2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -309,38 +386,29 @@ k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __r
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
         fa = addr.fetch(kt + 2, nk);
-        step_pipe<TM, TN>(st[0], st[1], fb, true, acc, f0, f1, wm, wn, lane, tid);
+        step_pipe<TM, TN, kT>(st[0], st[1], fb, true, acc, f0, f1, wm, wn, lane, tid);
         lds_barrier();
         read_frags<TM, TN>(st[1], f0, wm, wn, lane, 0);
         fb = addr.fetch(kt + 3, nk);
-        step_pipe<TM, TN>(st[1], st[0], fa, true, acc, f0, f1, wm, wn, lane, tid);
+        step_pipe<TM, TN, kT>(st[1], st[0], fa, true, acc, f0, f1, wm, wn, lane, tid);
         lds_barrier();
         read_frags<TM, TN>(st[0], f0, wm, wn, lane, 0);
     }
-    if (kt < nk) step_pipe<TM, TN>(st[0], st[1], fb, false, acc, f0, f1, wm, wn, lane, tid);
-    mfma_frags<TM, TN>(f1, acc);                       // sub-step 3 of the last step
+    if (kt < nk) step_pipe<TM, TN, kT>(st[0], st[1], fb, false, acc, f0, f1, wm, wn, lane, tid);
+    mfma_frags<TM, TN, kT>(f1, acc);                   // sub-step 3 of the last step
 
-    // epilogue: D element r of lane l sits at row 8*(r/4) + 4*(l/32) + r%4, column l%32
     const float alpha = (*sdA) * (*sdB);
-    const int lrow = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wn * TN * 32 + j * 32 + lrow;
-            if (col >= N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < M) {
-                    const float v = acc[i][j][r] * alpha;
-                    if constexpr (kBF16Out)
-                        reinterpret_cast<uint16_t*>(C)[row * ldc + col] = (uint16_t)f32_to_bf16(v);
-                    else
-                        reinterpret_cast<float*>(C)[row * ldc + col] = v;
-                }
-            }
-        }
+    const int64_t r0 = m0 + wm * TM * 32, c0 = n0 + wn * TN * 32;
+    if constexpr (kBF16Out) {
+        // staged through the (now idle) step buffers, 16 KiB per wave
+        const bool vec = (reinterpret_cast<uintptr_t>(C) & 15u) == 0 && (ldc * 2) % 16 == 0;
+        __syncthreads();                    // every wave has finished reading the step buffers
+        uint8_t* reg = reinterpret_cast<uint8_t*>(&st[0]) + wave * 16384;
+        epilogue_bf16<TM, TN>(acc, alpha, reg, lane, r0, c0, M, N, reinterpret_cast<uint16_t*>(C),
+                              ldc, vec);
+    } else {
+        epilogue_f32<TM, TN>(acc, alpha, lane, r0, c0, M, N, reinterpret_cast<float*>(C), ldc);
+    }
 }
 
 template <int WM, int WN, int TM, int TN>

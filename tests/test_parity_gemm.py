@@ -87,6 +87,27 @@ def test_gemm_zero_operand(nv, orc):
     assert torch.count_nonzero(c).item() == 0
 
 
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("off", [8, 3])
+def test_gemm_strided_output(nv, mx, dtype, off):
+    """C written into a column window of a wider matrix (row stride N + 40, first column at an
+    aligned (8) or unaligned (3) element offset): the window equals the contiguous result and
+    nothing outside it is touched."""
+    M, N, K = 300, 264, 256
+    a, b = W.act((M, K), 61).to(DEV), W.act((N, K), 62).to(DEV)
+    if mx:
+        qa, qb, gemm = nv.mx_quantize_1d(a), nv.mx_quantize_1d(b), nv.mx_gemm
+    else:
+        qa, qb, gemm = nv.quantize_1d(a), nv.quantize_1d(b), nv.gemm
+    ref = gemm(qa, qb, dtype)
+    big = torch.full((M, N + 40), -7.0, dtype=dtype, device=DEV)
+    gemm(qa, qb, dtype, out=big[:, off:off + N])
+    torch.cuda.synchronize()
+    assert torch.equal(big[:, off:off + N].cpu(), ref.cpu())
+    assert bool((big[:, :off] == -7.0).all()) and bool((big[:, off + N:] == -7.0).all())
+
+
 def _rows(M, n=256, seed=0):
     return np.sort(np.random.default_rng(seed).choice(M, n, replace=False))
 
