@@ -201,6 +201,16 @@ nvfp4_status nvfp4_qdq(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols
 nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
                                uint64_t seed, const nvfp4_tensor *out, void *stream);
 
+/* MXFP4 quantization of x^T, for the wgrad operands of the MXFP4 comparison [P3 NVFP4 in
+ * pratica]: x [T tokens x F features] (row stride ld) is read once and out [F x T] (layout
+ * MXFP4_BLK_1x32, out->rows = F, out->cols = T) receives, for every feature, its T values in
+ * 32-token blocks -- the same bytes as mxfp4_quantize_1d of the transposed matrix, SR element
+ * index feature * T + token included.  No Hadamard transform (that is part of the NVFP4 recipe).
+ * T % 32 == 0, F % 8 == 0 (else NVFP4_ERR_SHAPE); the grid limits of nvfp4_hadamard_quantize
+ * apply. */
+nvfp4_status mxfp4_quantize_1d_t(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
+                                 uint64_t seed, const nvfp4_tensor *out, void *stream);
+
 /* MXFP4 x MXFP4 GEMM, C = A * B^T with fp32 accumulation, both operands MXFP4_BLK_1x32. */
 nvfp4_status mxfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                         int64_t ldc, void *stream);

@@ -23,7 +23,7 @@ BLK_1x16, BLK_16x16, MX_1x32 = 0, 1, 2
 SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_quantize_1d",
            "nvfp4_quantize_2d", "nvfp4_hadamard_quantize", "nvfp4_dequantize", "nvfp4_gemm",
            "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual",
-           "nvfp4_quantize_1d_noise", "nvfp4_qdq")
+           "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t")
 
 
 class NvTensor(C.Structure):
@@ -56,6 +56,7 @@ def lib():
         L.nvfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.mxfp4_quantize_1d.argtypes = [P, i32, i64, i32, u64, T, P]
         L.mxfp4_gemm.argtypes = [T, T, P, i32, i64, P]
+        L.mxfp4_quantize_1d_t.argtypes = [P, i32, i64, i32, u64, T, P]
         L.nvfp4_dual_amax.argtypes = [P, i32, i64, i64, i64, u64, P, P, P]
         L.nvfp4_quantize_dual.argtypes = [P, i32, i64, u64, P, P, i32, u64, u64, T, T, P]
         L.nvfp4_quantize_1d_noise.argtypes = [P, i32, i64, P, i32, u64, T, P, P]
@@ -281,6 +282,17 @@ def mx_quantize_1d(x: torch.Tensor, rounding: int = RNE, seed: int = 0,
     d = q.desc()
     _check("mxfp4_quantize_1d", lib().mxfp4_quantize_1d(_ptr(x), dt, ld, rounding, seed, C.byref(d),
                                                         _stream(x.device)))
+    return q
+
+
+def mx_quantize_1d_t(x: torch.Tensor, rounding: int = RNE, seed: int = 0,
+                     out: QTensor | None = None) -> QTensor:
+    """x [T x F] -> MXFP4 of x^T [F x T] (32-token blocks), read once."""
+    x, dt, ld = _x(x)
+    q = QTensor.empty(x.shape[1], x.shape[0], MX_1x32, x.device) if out is None else out
+    d = q.desc()
+    _check("mxfp4_quantize_1d_t", lib().mxfp4_quantize_1d_t(_ptr(x), dt, ld, rounding, seed,
+                                                            C.byref(d), _stream(x.device)))
     return q
 
 

@@ -12,6 +12,9 @@
 // 16-point fast Walsh-Hadamard transforms.  A wave covers 8 feature groups (64 features, full
 // 128-byte rows on the read side) x 8 consecutive chunks (64 contiguous code bytes per feature
 // on the write side).
+//
+// The same tiling also serves the transposing MXFP4 quantizer of the comparison format (no
+// transform; 32-token blocks made of two adjacent chunks held by lanes l and l ^ 8).
 
 #include "device_codecs.hpp"
 #include "host_util.hpp"
@@ -388,6 +391,61 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
     quant_tile_transposed<T, kSR>(tile, rc, Tn, F, mask, tst, seed_t, codes_t, scales_t);
 }
 
+// MXFP4 quantization of x^T [P3 NVFP4 in pratica: MXFP4, 32-element blocks with power-of-two
+// scales, is the comparison format]: the 32 tokens of block b of feature f are chunks 2b and
+// 2b + 1, held by lanes l and l ^ 8 of one wave; the block amax is shared with one lane
+// exchange, E8M0 exponent floor(log2 amax) - 2 clamped to [-127, 127] (0 for an all-zero
+// block), codes E2M1 of x * 2^-exponent (RNE, or SR with element index f * T + t), each lane
+// writing its 8 code bytes and the even-chunk lane the scale byte.  T % 32 == 0, so both lanes
+// of a pair are valid or neither is.
+template <typename T, bool kSR>
+__global__ void __launch_bounds__(kRhtThreads)
+k_mx_quant_t(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t seed,
+             uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const RhtCoords rc = rht_coords(Tn, F);
+    if (!rc.valid) return;
+    Tile16x8<T> tile;
+    tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int64_t feat = rc.f0 + f;
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        m = fmaxf(m, __shfl_xor(m, 8));
+        int e8 = 0;
+        if (m > 0.0f) {
+            e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
+            e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
+        }
+        uint32_t lo, hi;
+        if constexpr (kSR) {
+            const uint64_t idx = (uint64_t)feat * (uint64_t)Tn + (uint64_t)rc.c * 16;
+            const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
+            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+            float z[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float ze = __builtin_amdgcn_ldexpf(v[e], -e8);
+                z[e] = ze + ze;
+            }
+            lo = e2m1_sr_pack8(z, a);
+            hi = e2m1_sr_pack8(z + 8, b);
+        } else {
+            float z[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) z[e] = __builtin_amdgcn_ldexpf(v[e], -e8);
+            lo = e2m1_rne_pack8(z);
+            hi = e2m1_rne_pack8(z + 8);
+        }
+        *reinterpret_cast<uint2*>(codes + feat * (Tn / 2) + rc.c * 8) = make_uint2(lo, hi);
+        if ((rc.c & 1) == 0) scales[feat * (Tn / 32) + rc.c / 2] = (uint8_t)(e8 + 127);
+    }
+}
+
 static dim3 rht_grid(int64_t T, int64_t F) {
     return dim3((unsigned)((F + kFeatPerBlock - 1) / kFeatPerBlock),
                 (unsigned)((T / 16 + kChunksPerBlock - 1) / kChunksPerBlock));
@@ -549,5 +607,30 @@ extern "C" nvfp4_status nvfp4_quantize_dual(const void* x, nvfp4_dtype dt, int64
         if (rnd == NVFP4_SR) NVFP4_DQ(float, true); else NVFP4_DQ(float, false);
     }
 #undef NVFP4_DQ
+    return launch_status();
+}
+
+extern "C" nvfp4_status mxfp4_quantize_1d_t(const void* x, nvfp4_dtype dt, int64_t ld,
+                                            nvfp4_round rnd, uint64_t seed,
+                                            const nvfp4_tensor* out, void* stream) {
+    nvfp4_status s = check_q(out, MXFP4_BLK_1x32, false);
+    if (s) return s;
+    const int64_t F = out->rows, T = out->cols;
+    s = check_rht_input(x, dt, T, F, ld);
+    if (s) return s;
+    if (T % 32 != 0) return NVFP4_ERR_SHAPE;
+    if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
+    if (T == 0 || F == 0) return NVFP4_OK;
+    const dim3 grid = rht_grid(T, F), block(kRhtThreads);
+    hipStream_t st = as_stream(stream);
+#define NVFP4_MXT(TT, SRV)                                                                        \
+    hipLaunchKernelGGL((k_mx_quant_t<TT, SRV>), grid, block, 0, st, static_cast<const TT*>(x), T, \
+                       F, ld, seed, out->codes, out->scales)
+    if (dt == NVFP4_BF16) {
+        if (rnd == NVFP4_SR) NVFP4_MXT(uint16_t, true); else NVFP4_MXT(uint16_t, false);
+    } else {
+        if (rnd == NVFP4_SR) NVFP4_MXT(float, true); else NVFP4_MXT(float, false);
+    }
+#undef NVFP4_MXT
     return launch_status();
 }

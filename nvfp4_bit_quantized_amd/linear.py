@@ -17,12 +17,19 @@ forward pass rounds to nearest, backward and update passes round stochastically)
             random signs so that the transform cancels in the product.
 Every one of these steps runs in the HIP library; this file only allocates outputs and passes
 pointers.  Shapes: T, in and out multiples of 16.
+
+The MXFP4 comparison format ("I ricercatori di Nvidia ...", NVFP4 in pratica: MXFP4 needed more
+training data to match NVFP4) runs the same three GEMMs with every operand in MXFP4 (32-element
+blocks, power-of-two scales applied by the matrix core), the same rounding per pass, and plain
+transposes instead of the Hadamard transform, which belongs to the NVFP4 recipe.  Shapes there:
+T, in and out multiples of 32.
 """
 from __future__ import annotations
 
 import torch
 
-from . import RNE, SR, gemm, quantize_1d, quantize_2d, quantize_dual
+from . import (RNE, SR, gemm, mx_gemm, mx_quantize_1d, mx_quantize_1d_t, quantize_1d, quantize_2d,
+               quantize_dual)
 
 _MASK64 = (1 << 64) - 1
 
@@ -66,20 +73,56 @@ class NVFP4LinearFn(torch.autograd.Function):
         return dx, dw, None, None, None
 
 
+class MXFP4LinearFn(torch.autograd.Function):
+    """y = x W^T with every GEMM operand in MXFP4 and fp32 accumulation (the comparison format).
+    forward   x, W -> MXFP4 row-wise (RNE); y = mx_gemm(x_q, W_q); when a gradient will be
+              needed, W^T [in x out] and x^T [in x T] are quantized (RNE) from one read each
+    backward  dY -> MXFP4 row-wise (SR, dgrad seed) and dY^T [out x T] (SR, wgrad seed);
+              dx = mx_gemm(dY_q, W^T_q), dW = mx_gemm(dY^T_q, x^T_q)."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, seed_dgrad: int, seed_wgrad: int):
+        need_grad = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+        y = mx_gemm(mx_quantize_1d(x, RNE), mx_quantize_1d(w, RNE), x.dtype)
+        ctx.q = (mx_quantize_1d_t(x, RNE), mx_quantize_1d_t(w, RNE)) if need_grad else None
+        ctx.seeds = (seed_dgrad, seed_wgrad)
+        ctx.dtypes = (x.dtype, w.dtype)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        qxt, qwt = ctx.q
+        seed_dgrad, seed_wgrad = ctx.seeds
+        x_dt, w_dt = ctx.dtypes
+        dy = dy.contiguous()
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            dx = mx_gemm(mx_quantize_1d(dy, SR, seed_dgrad), qwt, x_dt)
+        if ctx.needs_input_grad[1]:
+            dw = mx_gemm(mx_quantize_1d_t(dy, SR, seed_wgrad), qxt, w_dt)
+        ctx.q = None
+        return dx, dw, None, None
+
+
 class NVFP4Linear(torch.nn.Module):
     """Linear layer without bias, W [out x in] in bf16 or fp32.
 
     high_precision=False: the NVFP4 path above.  high_precision=True: the layer stays in its own
-    dtype (torch's linear), the selective-precision part of the recipe.  ``sign_seed`` fixes the
-    layer's random Hadamard signs; the stochastic-rounding seeds of each backward pass derive
-    from ``seed`` and a per-layer call counter, so runs are reproducible."""
+    dtype (torch's linear), the selective-precision part of the recipe.  fmt="mxfp4" runs the
+    MXFP4 comparison format instead of NVFP4.  ``sign_seed`` fixes the layer's random Hadamard
+    signs; the stochastic-rounding seeds of each backward pass derive from ``seed`` and a
+    per-layer call counter, so runs are reproducible."""
 
     def __init__(self, in_features: int, out_features: int, high_precision: bool = False,
                  dtype: torch.dtype = torch.bfloat16, device="cuda", seed: int = 0,
-                 sign_seed: int | None = None):
+                 sign_seed: int | None = None, fmt: str = "nvfp4"):
         super().__init__()
-        if in_features % 16 or out_features % 16:
-            raise ValueError("NVFP4Linear needs in_features and out_features divisible by 16")
+        if fmt not in ("nvfp4", "mxfp4"):
+            raise ValueError("fmt must be 'nvfp4' or 'mxfp4'")
+        self.fmt, self.align = fmt, 16 if fmt == "nvfp4" else 32
+        if in_features % self.align or out_features % self.align:
+            raise ValueError(f"NVFP4Linear ({fmt}) needs in_features and out_features divisible "
+                             f"by {self.align}")
         self.in_features, self.out_features = in_features, out_features
         self.high_precision = high_precision
         self.weight = torch.nn.Parameter(torch.empty((out_features, in_features), dtype=dtype,
@@ -94,17 +137,21 @@ class NVFP4Linear(torch.nn.Module):
         if self.high_precision:
             y = torch.nn.functional.linear(x2, self.weight)
         else:
-            if x2.shape[0] % 16:
-                raise ValueError("NVFP4Linear needs the token count divisible by 16")
+            if x2.shape[0] % self.align:
+                raise ValueError(f"NVFP4Linear ({self.fmt}) needs the token count divisible by "
+                                 f"{self.align}")
             x2 = x2.contiguous()
             s_d, s_w = _mix(self.seed, 2 * self.calls), _mix(self.seed, 2 * self.calls + 1)
             self.calls += 1
-            y = NVFP4LinearFn.apply(x2, self.weight, self.sign_seed, s_d, s_w)
+            if self.fmt == "mxfp4":
+                y = MXFP4LinearFn.apply(x2, self.weight, s_d, s_w)
+            else:
+                y = NVFP4LinearFn.apply(x2, self.weight, self.sign_seed, s_d, s_w)
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:
-        mode = "bf16" if self.high_precision else "nvfp4"
+        mode = "bf16" if self.high_precision else self.fmt
         return f"in={self.in_features}, out={self.out_features}, {mode}"
 
 
-__all__ = ["NVFP4LinearFn", "NVFP4Linear"]
+__all__ = ["NVFP4LinearFn", "MXFP4LinearFn", "NVFP4Linear"]

@@ -94,6 +94,21 @@ def test_gemm_validation(L):
     assert L.mxfp4_quantize_1d(FAKE, nv.BF16, 48, nv.RNE, 0, C.byref(mxa), None) == nv.ERR_SHAPE
 
 
+def test_mx_transposed_validation(L):
+    # out [F x T] = [64 x 96]: x is [96 x 64]
+    q = _q(64, 96, layout=nv.MX_1x32)
+    assert L.mxfp4_quantize_1d_t(FAKE, nv.BF16, 64, 2, 0, C.byref(q), None) == nv.ERR_DTYPE
+    assert L.mxfp4_quantize_1d_t(FAKE, nv.BF16, 32, nv.RNE, 0, C.byref(q), None) == nv.ERR_SHAPE
+    assert L.mxfp4_quantize_1d_t(None, nv.BF16, 64, nv.RNE, 0, C.byref(q), None) == nv.ERR_NULL
+    assert L.mxfp4_quantize_1d_t(FAKE, nv.BF16, 64, nv.RNE, 0, None, None) == nv.ERR_NULL
+    odd = _q(60, 96, layout=nv.MX_1x32)                      # F % 8 != 0
+    assert L.mxfp4_quantize_1d_t(FAKE, nv.BF16, 64, nv.RNE, 0, C.byref(odd), None) == nv.ERR_SHAPE
+    short = _q(64, 32 * 3 + 16, layout=nv.MX_1x32)            # T % 32 != 0 fails the layout check
+    assert L.mxfp4_quantize_1d_t(FAKE, nv.BF16, 64, nv.RNE, 0, C.byref(short), None) == nv.ERR_SHAPE
+    nv_layout = _q(64, 96)
+    assert L.mxfp4_quantize_1d_t(FAKE, nv.BF16, 64, nv.RNE, 0, C.byref(nv_layout), None) == nv.ERR_LAYOUT
+
+
 def test_dequantize_validation(L):
     q = _q(16, 32)
     assert L.nvfp4_dequantize(C.byref(q), None, nv.F32, 32, None) == nv.ERR_NULL

@@ -1,5 +1,6 @@
-"""The NVFP4 linear layer (autograd Function over the C ABI) against the CPU oracle, the BF16
-flag against torch's linear, and an FFN pair against its BF16 counterpart (numeric error only).
+"""The NVFP4 linear layer (autograd Function over the C ABI) and its MXFP4 comparison mode against
+the CPU oracle, the BF16 flag against torch's linear, and an FFN pair against its BF16 counterpart
+(numeric error only).
 
 Parity: y = x W^T, dx = dy W and dW = dy^T x from the layer must match the oracle's float64 GEMMs
 on the oracle's own quantized operands (1D RNE for x, 16x16 tiles for W and its transposed copy,
@@ -57,6 +58,42 @@ def test_linear_matches_oracle(L, orc, T, fin, fout):
     assert _rel(y.detach().cpu().numpy(), y_ref) <= 1e-5
     assert _rel(xd.grad.cpu().numpy(), dx_ref) <= 1e-5
     assert _rel(wd.grad.cpu().numpy(), dw_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("T,fin,fout", [(64, 128, 96), (256, 96, 64)])
+def test_mx_linear_matches_oracle(L, orc, T, fin, fout):
+    """The MXFP4 comparison mode: every operand MXFP4 (x, W row-wise RNE; dY row-wise SR at the
+    dgrad seed; W^T, x^T RNE and dY^T SR at the wgrad seed, plain transposes)."""
+    x = W.act((T, fin), 31).float()
+    w = W.weight((fout, fin), 32).float()
+    dy = W.grad((T, fout), 33).float()
+    sd, sw = 0x5EED0013, 0x5EED0014
+    xd = x.to(DEV).requires_grad_(True)
+    wd = w.to(DEV).requires_grad_(True)
+    y = L.MXFP4LinearFn.apply(xd, wd, sd, sw)
+    y.backward(dy.to(DEV))
+    xb, wb, dyb = W.bits(x), W.bits(w), W.bits(dy)
+    tr = lambda a: np.ascontiguousarray(a.T)
+    y_ref = orc.mx_gemm_f64(orc.mx_quantize_1d(xb), orc.mx_quantize_1d(wb), T, fout, fin)
+    dx_ref = orc.mx_gemm_f64(orc.mx_quantize_1d(dyb, 1, sd), orc.mx_quantize_1d(tr(wb)),
+                             T, fin, fout)
+    dw_ref = orc.mx_gemm_f64(orc.mx_quantize_1d(tr(dyb), 1, sw), orc.mx_quantize_1d(tr(xb)),
+                             fout, fin, T)
+    assert _rel(y.detach().cpu().numpy(), y_ref) <= 1e-5
+    assert _rel(xd.grad.cpu().numpy(), dx_ref) <= 1e-5
+    assert _rel(wd.grad.cpu().numpy(), dw_ref) <= 1e-5
+
+
+def test_mx_module_shapes(L):
+    with pytest.raises(ValueError):
+        L.NVFP4Linear(48, 64, fmt="mxfp4")
+    m = L.NVFP4Linear(64, 96, fmt="mxfp4", seed=3)
+    with torch.no_grad():
+        m.weight.copy_(W.weight((96, 64), 34).to(DEV))
+    with pytest.raises(ValueError):
+        m(W.act((48, 64), 35).to(DEV))
+    y = m(W.act((2, 32, 64), 36).to(DEV))
+    assert y.shape == (2, 32, 96)
 
 
 def test_high_precision_flag_is_torch_linear(L):
