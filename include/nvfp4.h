@@ -37,6 +37,14 @@
 
 #include <stdint.h>
 
+/* Only the functions declared here are exported from the library; everything else it
+ * contains (kernels, helpers) is built with hidden visibility. */
+#if defined(__GNUC__) || defined(__clang__)
+#define NVFP4_API __attribute__((visibility("default")))
+#else
+#define NVFP4_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -81,23 +89,23 @@ typedef struct {
 } nvfp4_tensor;
 
 /* Human-readable text for a status code (static storage). */
-const char *nvfp4_status_string(nvfp4_status s);
+NVFP4_API const char *nvfp4_status_string(nvfp4_status s);
 
 /* Per-tensor amax: *amax_out = max |x| over x [rows x cols] (row stride ld).  This is the first
  * level of the two-level scaling [P3 Come funziona NVFP4?].  amax_out is overwritten. */
-nvfp4_status nvfp4_amax(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+NVFP4_API nvfp4_status nvfp4_amax(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                         float *amax_out, void *stream);
 
 /* amax of the random-Hadamard-transformed tensor (see nvfp4_hadamard_quantize), without
  * writing the transform: x is [T tokens x F features], T % 16 == 0. */
-nvfp4_status nvfp4_hadamard_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
+NVFP4_API nvfp4_status nvfp4_hadamard_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
                                  uint64_t sign_seed, float *amax_out, void *stream);
 
 /* 1D NVFP4 quantization of x [out->rows x out->cols] (row stride ld) into `out`
  * (layout NVFP4_BLK_1x16, cols % 16 == 0) [P1 Caracteristicas; P2 Describir].
  * amax_in: device pointer to the tensor amax to use, or NULL to compute it first (two passes).
  * Writes out->codes, out->scales, *out->amax (= the amax used) and *out->s_dec. */
-nvfp4_status nvfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, const float *amax_in,
+NVFP4_API nvfp4_status nvfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, const float *amax_in,
                                nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
                                void *stream);
 
@@ -111,7 +119,7 @@ nvfp4_status nvfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, const 
  * atomics: the order of the additions, and so the last bits of the sums, vary from run to run;
  * codes and scales are exactly those of nvfp4_quantize_1d.  A tensor treated as zero (amax below
  * 2^-100) reports sums of its fp32 squares, which may underflow to 0. */
-nvfp4_status nvfp4_quantize_1d_noise(const void *x, nvfp4_dtype dt, int64_t ld, const float *amax_in,
+NVFP4_API nvfp4_status nvfp4_quantize_1d_noise(const void *x, nvfp4_dtype dt, int64_t ld, const float *amax_in,
                                      nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
                                      double *sums, void *stream);
 
@@ -121,7 +129,7 @@ nvfp4_status nvfp4_quantize_1d_noise(const void *x, nvfp4_dtype dt, int64_t ld, 
  * the same quantized values transposed, [cols x rows], layout NVFP4_BLK_16x16 -- the dgrad
  * operand.  Both share amax and s_dec values (out_t's amax/s_dec pointers are written too if
  * they are non-NULL). */
-nvfp4_status nvfp4_quantize_2d(const void *w, nvfp4_dtype dt, int64_t ld, const float *amax_in,
+NVFP4_API nvfp4_status nvfp4_quantize_2d(const void *w, nvfp4_dtype dt, int64_t ld, const float *amax_in,
                                const nvfp4_tensor *out, const nvfp4_tensor *out_t, void *stream);
 
 /* Random Hadamard transform + transpose + 1D quantization of a wgrad operand
@@ -132,14 +140,14 @@ nvfp4_status nvfp4_quantize_2d(const void *w, nvfp4_dtype dt, int64_t ld, const 
  * out is [F x T] (out->rows = F, out->cols = T, layout NVFP4_BLK_1x16), so the token dimension
  * is the contiguous K of the wgrad GEMM and each 16-token chunk is one NVFP4 block.
  * amax_in: the amax of the TRANSFORMED tensor, or NULL to compute it. */
-nvfp4_status nvfp4_hadamard_quantize(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
+NVFP4_API nvfp4_status nvfp4_hadamard_quantize(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
                                      const float *amax_in, nvfp4_round rnd, uint64_t seed,
                                      const nvfp4_tensor *out, void *stream);
 
 /* amax of x [T x F] and of its random Hadamard transform (as in nvfp4_hadamard_quantize) in one
  * read of x: *amax_out = max |x|, *amax_t_out = max |(1/4) H16 D x|.  T % 16 == 0, F % 8 == 0;
  * the two outputs must be distinct (else NVFP4_ERR_SHAPE). */
-nvfp4_status nvfp4_dual_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
+NVFP4_API nvfp4_status nvfp4_dual_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
                              uint64_t sign_seed, float *amax_out, float *amax_t_out, void *stream);
 
 /* Fused dual-orientation quantization: one read of an activation or gradient x [T tokens x
@@ -157,14 +165,14 @@ nvfp4_status nvfp4_dual_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F
  * A supplied amax is never overwritten before it is used, even when it is out's own slot.
  * Requirements:
  * T % 16 == 0, F % 16 == 0; out and out_t have distinct amax and s_dec pointers. */
-nvfp4_status nvfp4_quantize_dual(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
+NVFP4_API nvfp4_status nvfp4_quantize_dual(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
                                  const float *amax_in, const float *amax_t_in, nvfp4_round rnd,
                                  uint64_t seed, uint64_t seed_t, const nvfp4_tensor *out,
                                  const nvfp4_tensor *out_t, void *stream);
 
 /* Dequantize an NVFP4 tensor (1x16 or 16x16): y = fl(fl(v * scale_b) * s_dec) in fp32, stored
  * as fp32 or rounded to nearest-even bf16.  y is [q->rows x q->cols], row stride ld. */
-nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dtype dt, int64_t ld,
+NVFP4_API nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dtype dt, int64_t ld,
                               void *stream);
 
 /* NVFP4 x NVFP4 GEMM with fp32 accumulation [P2 Describir: weights, activations and gradients
@@ -172,7 +180,7 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dtype dt, in
  *   C[m,n] = s_dA * s_dB * sum_k (vA * sA) * (vB * sB),
  * stored fp32 or bf16 (round to nearest even) into c [M x N] with row stride ldc.
  * Requirements: a->cols == b->cols == K, K % 16 == 0; c need only be element-aligned. */
-nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
+NVFP4_API nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                         int64_t ldc, void *stream);
 
 /* Format sweep [P2 Describir: block size, scale format and rounding method are the FP4 design
@@ -189,7 +197,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, n
  * sums (optional, two doubles, overwritten): sum x^2 and sum (y - x)^2, accumulated in fp64 with
  * device atomics (run-dependent order in the last bits).  Unknown block or format:
  * NVFP4_ERR_SHAPE / NVFP4_ERR_DTYPE. */
-nvfp4_status nvfp4_qdq(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+NVFP4_API nvfp4_status nvfp4_qdq(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                        int32_t block, int32_t scale_fmt, const float *amax_in, nvfp4_round rnd,
                        uint64_t seed, float *y, int64_t ldy, float *amax_out, double *sums,
                        void *stream);
@@ -198,7 +206,7 @@ nvfp4_status nvfp4_qdq(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols
  * cols with an E8M0 scale 2^(floor(log2 amax_b) - 2) (byte = exponent + 127, clamped to
  * [0, 254]; an all-zero block gets byte 127); codes E2M1 of x * 2^-exponent, RNE or SR as above.
  * out: layout MXFP4_BLK_1x32, cols % 32 == 0; amax/s_dec are not used. */
-nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
+NVFP4_API nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
                                uint64_t seed, const nvfp4_tensor *out, void *stream);
 
 /* MXFP4 quantization of x^T, for the wgrad operands of the MXFP4 comparison [P3 NVFP4 in
@@ -208,11 +216,11 @@ nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_
  * index feature * T + token included.  No Hadamard transform (that is part of the NVFP4 recipe).
  * T % 32 == 0, F % 8 == 0 (else NVFP4_ERR_SHAPE); the grid limits of nvfp4_hadamard_quantize
  * apply. */
-nvfp4_status mxfp4_quantize_1d_t(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
+NVFP4_API nvfp4_status mxfp4_quantize_1d_t(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
                                  uint64_t seed, const nvfp4_tensor *out, void *stream);
 
 /* MXFP4 x MXFP4 GEMM, C = A * B^T with fp32 accumulation, both operands MXFP4_BLK_1x32. */
-nvfp4_status mxfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
+NVFP4_API nvfp4_status mxfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                         int64_t ldc, void *stream);
 
 #ifdef __cplusplus

@@ -1,7 +1,8 @@
 """Build ``libnvfp4.so`` from the HIP sources in ``csrc/`` with hipcc for gfx950.
 
 Every source is compiled with -ffp-contract=off (the quantizers must perform single IEEE fp32
-operations) and with packed-fp32 instructions disabled.
+operations), with packed-fp32 instructions disabled, and with hidden visibility, and linked
+with a version script (csrc/exports.map): the library exports exactly the C ABI.
 """
 from __future__ import annotations
 
@@ -15,8 +16,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libnvfp4.so")
 SOURCES = ["quantize.hip", "hadamard.hip", "gemm.hip", "gemm_mx.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+         "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 
 
 def _compile(src: str) -> str:
@@ -30,7 +31,9 @@ def build() -> str:
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
+                    "-Wl,--version-script=" + os.path.join(CSRC, "exports.map"), "-o", tmp, *objs],
+                   check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

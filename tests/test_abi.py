@@ -33,6 +33,21 @@ def test_exports_every_declared_function(L):
     assert set(names) == set(nv.SYMBOLS)
 
 
+def test_exports_nothing_else(L):
+    """The dynamic symbol table holds exactly the declared functions (kernel handles and helpers
+    are local), read from the ELF file with the system's nm."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", nv.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    syms -= {"_init", "_fini"}
+    assert syms == set(_declared()), sorted(syms ^ set(_declared()))
+
+
 def test_status_strings(L):
     for s in range(7):
         assert L.nvfp4_status_string(s)
