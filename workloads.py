@@ -43,6 +43,34 @@ def normal(shape, sigma: float, seed: int, spike_frac: float = 0.0, spike_mult: 
     return _finish(v, shape, dtype)
 
 
+def edge_fp32(kind: str, shape, seed: int) -> torch.Tensor:
+    """fp32 tensors at the edges of the formats' ranges (the degenerate cases of the method):
+      "tiny"       N(0,1) * 1e-38: fp32 subnormals, amax below the 2^-100 zero threshold
+      "near_zero"  N(0,1) * 1e-29: amax just above that threshold (huge tensor scale factors)
+      "huge"       N(0,1) * 1e37: amax near the top of the fp32 range
+      "wide"       random signs times 2^u, u uniform in [-70, 12): blocks whose E4M3 scale is
+                   subnormal or zero next to blocks with large values
+      "signed_zeros" mostly +0 and -0, with 1% N(0,1) entries."""
+    rng = _rng(seed)
+    n = int(np.prod(shape))
+    if kind == "tiny":
+        v = rng.standard_normal(n) * 1e-38
+    elif kind == "near_zero":
+        v = rng.standard_normal(n) * 1e-29
+    elif kind == "huge":
+        v = rng.standard_normal(n) * 1e37
+    elif kind == "wide":
+        v = np.where(rng.random(n) < 0.5, -1.0, 1.0) * np.exp2(rng.uniform(-70.0, 12.0, n))
+    elif kind == "signed_zeros":
+        v = np.where(rng.random(n) < 0.5, -0.0, 0.0)
+        k = n // 100
+        if k > 0:
+            v[rng.choice(n, k, replace=False)] = rng.standard_normal(k)
+    else:
+        raise ValueError(kind)
+    return _finish(v, shape, torch.float32)
+
+
 def student_t(shape, nu: float, seed: int, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     rng = _rng(seed)
     n = int(np.prod(shape))
