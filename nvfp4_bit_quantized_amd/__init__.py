@@ -92,7 +92,13 @@ def _dtype_code(t: torch.dtype) -> int:
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
-    return None if t is None else t.data_ptr()
+    """Device address of a GPU tensor; a host tensor is refused here, since a kernel handed a host
+    address would fault instead of returning an error."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+    return t.data_ptr()
 
 
 @dataclass

@@ -194,3 +194,13 @@ def test_launch_limits_are_rejected(L):
     h = _q(16, T)
     assert L.nvfp4_hadamard_quantize(FAKE, nv.BF16, 16, 1, None, nv.RNE, 0, C.byref(h), None) == nv.ERR_SHAPE
 
+
+
+def test_binding_refuses_host_tensors():
+    """Host tensors never reach the library (their addresses would fault on the device)."""
+    import torch
+    x = torch.zeros((16, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        nv._ptr(x)
+    with pytest.raises(ValueError):
+        nv.quantize_1d(x)
