@@ -22,7 +22,8 @@
  *     element code is E2M1(x * (2688 / A) / scale_b).  The value of a code is v * scale_b * s_dec.
  *
  * Conventions for every entry point:
- *   - All pointers are DEVICE pointers owned by the caller, 16-byte aligned; the library never
+ *   - All pointers are DEVICE pointers owned by the caller, 16-byte aligned (GEMM outputs need
+ *     only element alignment, and amax / s_dec 4-byte alignment); the library never
  *     allocates or frees memory and keeps no state between calls, so calls on different streams
  *     are independent.  `stream` is a hipStream_t (NULL = the default stream).
  *   - Work is enqueued on `stream` and the call returns without synchronising the host.
@@ -94,20 +95,20 @@ NVFP4_API const char *nvfp4_status_string(nvfp4_status s);
 /* Per-tensor amax: *amax_out = max |x| over x [rows x cols] (row stride ld).  This is the first
  * level of the two-level scaling [P3 Come funziona NVFP4?].  amax_out is overwritten. */
 NVFP4_API nvfp4_status nvfp4_amax(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
-                        float *amax_out, void *stream);
+                                  float *amax_out, void *stream);
 
 /* amax of the random-Hadamard-transformed tensor (see nvfp4_hadamard_quantize), without
  * writing the transform: x is [T tokens x F features], T % 16 == 0. */
 NVFP4_API nvfp4_status nvfp4_hadamard_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
-                                 uint64_t sign_seed, float *amax_out, void *stream);
+                                           uint64_t sign_seed, float *amax_out, void *stream);
 
 /* 1D NVFP4 quantization of x [out->rows x out->cols] (row stride ld) into `out`
  * (layout NVFP4_BLK_1x16, cols % 16 == 0) [P1 Caracteristicas; P2 Describir].
  * amax_in: device pointer to the tensor amax to use, or NULL to compute it first (two passes).
  * Writes out->codes, out->scales, *out->amax (= the amax used) and *out->s_dec. */
 NVFP4_API nvfp4_status nvfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, const float *amax_in,
-                               nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
-                               void *stream);
+                                         nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
+                                         void *stream);
 
 /* nvfp4_quantize_1d plus, in the same pass, the quantization-noise diagnostic of
  * [P2 Describir: quantized training loses efficiency once the gradient norm falls below about
@@ -120,8 +121,8 @@ NVFP4_API nvfp4_status nvfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t 
  * codes and scales are exactly those of nvfp4_quantize_1d.  A tensor treated as zero (amax below
  * 2^-100) reports sums of its fp32 squares, which may underflow to 0. */
 NVFP4_API nvfp4_status nvfp4_quantize_1d_noise(const void *x, nvfp4_dtype dt, int64_t ld, const float *amax_in,
-                                     nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
-                                     double *sums, void *stream);
+                                               nvfp4_round rnd, uint64_t seed, const nvfp4_tensor *out,
+                                               double *sums, void *stream);
 
 /* 2D NVFP4 quantization of a weight w [out->rows x out->cols] with one E4M3 scale per 16x16
  * tile, round to nearest [P1 Metodologia: two-dimensional block scaling for weights].
@@ -130,7 +131,7 @@ NVFP4_API nvfp4_status nvfp4_quantize_1d_noise(const void *x, nvfp4_dtype dt, in
  * operand.  Both share amax and s_dec values (out_t's amax/s_dec pointers are written too if
  * they are non-NULL). */
 NVFP4_API nvfp4_status nvfp4_quantize_2d(const void *w, nvfp4_dtype dt, int64_t ld, const float *amax_in,
-                               const nvfp4_tensor *out, const nvfp4_tensor *out_t, void *stream);
+                                         const nvfp4_tensor *out, const nvfp4_tensor *out_t, void *stream);
 
 /* Random Hadamard transform + transpose + 1D quantization of a wgrad operand
  * [P1 Metodologia: random Hadamard transforms].  x is [T tokens x F features] (row stride ld);
@@ -141,14 +142,14 @@ NVFP4_API nvfp4_status nvfp4_quantize_2d(const void *w, nvfp4_dtype dt, int64_t 
  * is the contiguous K of the wgrad GEMM and each 16-token chunk is one NVFP4 block.
  * amax_in: the amax of the TRANSFORMED tensor, or NULL to compute it. */
 NVFP4_API nvfp4_status nvfp4_hadamard_quantize(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
-                                     const float *amax_in, nvfp4_round rnd, uint64_t seed,
-                                     const nvfp4_tensor *out, void *stream);
+                                               const float *amax_in, nvfp4_round rnd, uint64_t seed,
+                                               const nvfp4_tensor *out, void *stream);
 
 /* amax of x [T x F] and of its random Hadamard transform (as in nvfp4_hadamard_quantize) in one
  * read of x: *amax_out = max |x|, *amax_t_out = max |(1/4) H16 D x|.  T % 16 == 0, F % 8 == 0;
  * the two outputs must be distinct (else NVFP4_ERR_SHAPE). */
 NVFP4_API nvfp4_status nvfp4_dual_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
-                             uint64_t sign_seed, float *amax_out, float *amax_t_out, void *stream);
+                                       uint64_t sign_seed, float *amax_out, float *amax_t_out, void *stream);
 
 /* Fused dual-orientation quantization: one read of an activation or gradient x [T tokens x
  * F features] (row stride ld) writes both NVFP4 copies a training step takes from it
@@ -166,14 +167,14 @@ NVFP4_API nvfp4_status nvfp4_dual_amax(const void *x, nvfp4_dtype dt, int64_t T,
  * Requirements:
  * T % 16 == 0, F % 16 == 0; out and out_t have distinct amax and s_dec pointers. */
 NVFP4_API nvfp4_status nvfp4_quantize_dual(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
-                                 const float *amax_in, const float *amax_t_in, nvfp4_round rnd,
-                                 uint64_t seed, uint64_t seed_t, const nvfp4_tensor *out,
-                                 const nvfp4_tensor *out_t, void *stream);
+                                           const float *amax_in, const float *amax_t_in, nvfp4_round rnd,
+                                           uint64_t seed, uint64_t seed_t, const nvfp4_tensor *out,
+                                           const nvfp4_tensor *out_t, void *stream);
 
 /* Dequantize an NVFP4 tensor (1x16 or 16x16): y = fl(fl(v * scale_b) * s_dec) in fp32, stored
  * as fp32 or rounded to nearest-even bf16.  y is [q->rows x q->cols], row stride ld. */
 NVFP4_API nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dtype dt, int64_t ld,
-                              void *stream);
+                                        void *stream);
 
 /* NVFP4 x NVFP4 GEMM with fp32 accumulation [P2 Describir: weights, activations and gradients
  * all in FP4]: C = A * B^T, A [M x K] (layout 1x16), B [N x K] (layout 1x16 or 16x16),
@@ -181,7 +182,7 @@ NVFP4_API nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dt
  * stored fp32 or bf16 (round to nearest even) into c [M x N] with row stride ldc.
  * Requirements: a->cols == b->cols == K, K % 16 == 0; c need only be element-aligned. */
 NVFP4_API nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
-                        int64_t ldc, void *stream);
+                                  int64_t ldc, void *stream);
 
 /* Format sweep [P2 Describir: block size, scale format and rounding method are the FP4 design
  * choices explored, and 16-element blocks with E4M3 scales (NVFP4) come out best]: quantize
@@ -198,16 +199,16 @@ NVFP4_API nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, 
  * device atomics (run-dependent order in the last bits).  Unknown block or format:
  * NVFP4_ERR_SHAPE / NVFP4_ERR_DTYPE. */
 NVFP4_API nvfp4_status nvfp4_qdq(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
-                       int32_t block, int32_t scale_fmt, const float *amax_in, nvfp4_round rnd,
-                       uint64_t seed, float *y, int64_t ldy, float *amax_out, double *sums,
-                       void *stream);
+                                 int32_t block, int32_t scale_fmt, const float *amax_in, nvfp4_round rnd,
+                                 uint64_t seed, float *y, int64_t ldy, float *amax_out, double *sums,
+                                 void *stream);
 
 /* MXFP4 quantization (the comparison format of [P3 NVFP4 in pratica]): 32-element blocks along
  * cols with an E8M0 scale 2^(floor(log2 amax_b) - 2) (byte = exponent + 127, clamped to
  * [0, 254]; an all-zero block gets byte 127); codes E2M1 of x * 2^-exponent, RNE or SR as above.
  * out: layout MXFP4_BLK_1x32, cols % 32 == 0; amax/s_dec are not used. */
 NVFP4_API nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
-                               uint64_t seed, const nvfp4_tensor *out, void *stream);
+                                         uint64_t seed, const nvfp4_tensor *out, void *stream);
 
 /* MXFP4 quantization of x^T, for the wgrad operands of the MXFP4 comparison [P3 NVFP4 in
  * pratica]: x [T tokens x F features] (row stride ld) is read once and out [F x T] (layout
@@ -217,11 +218,11 @@ NVFP4_API nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t 
  * T % 32 == 0, F % 8 == 0 (else NVFP4_ERR_SHAPE); the grid limits of nvfp4_hadamard_quantize
  * apply. */
 NVFP4_API nvfp4_status mxfp4_quantize_1d_t(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
-                                 uint64_t seed, const nvfp4_tensor *out, void *stream);
+                                           uint64_t seed, const nvfp4_tensor *out, void *stream);
 
 /* MXFP4 x MXFP4 GEMM, C = A * B^T with fp32 accumulation, both operands MXFP4_BLK_1x32. */
 NVFP4_API nvfp4_status mxfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
-                        int64_t ldc, void *stream);
+                                  int64_t ldc, void *stream);
 
 #ifdef __cplusplus
 }
