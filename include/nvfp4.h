@@ -180,7 +180,8 @@ NVFP4_API nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dt
  * all in FP4]: C = A * B^T, A [M x K] (layout 1x16), B [N x K] (layout 1x16 or 16x16),
  *   C[m,n] = s_dA * s_dB * sum_k (vA * sA) * (vB * sB),
  * stored fp32 or bf16 (round to nearest even) into c [M x N] with row stride ldc.
- * Requirements: a->cols == b->cols == K, K % 16 == 0; c need only be element-aligned. */
+ * Requirements: a->cols == b->cols == K, K % 16 == 0; c need only be element-aligned.
+ * K == 0 writes zeros (the empty sum) and reads neither operand's codes nor scales. */
 NVFP4_API nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                                   int64_t ldc, void *stream);
 
@@ -220,7 +221,9 @@ NVFP4_API nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t 
 NVFP4_API nvfp4_status mxfp4_quantize_1d_t(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
                                            uint64_t seed, const nvfp4_tensor *out, void *stream);
 
-/* MXFP4 x MXFP4 GEMM, C = A * B^T with fp32 accumulation, both operands MXFP4_BLK_1x32. */
+/* MXFP4 x MXFP4 GEMM, C = A * B^T with fp32 accumulation, both operands MXFP4_BLK_1x32, stored
+ * fp32 or bf16 (round to nearest even) into c [M x N] with row stride ldc.  Requirements as for
+ * nvfp4_gemm with K % 32 == 0 (s_dec and amax are not used); K == 0 writes zeros. */
 NVFP4_API nvfp4_status mxfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                                   int64_t ldc, void *stream);
 

@@ -6,63 +6,241 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 applies in hardware, so packed codes go to the matrix core
 // without any unpacking:
 //   C[m,n] = sum_kb 2^(eA[m,kb] + eB[n,kb]) * sum_{k in kb} vA[m,k] * vB[n,k].
-// One MFMA covers K = 64: lane l supplies row l%32 and the 32-element block (l/32) of the
-// 64, i.e. 16 bytes of codes plus that block's E8M0 byte.
+// One MFMA covers K = 64: lane l supplies row l%32 and the 32-element block (l/32) of the 64,
+// i.e. 16 bytes of codes plus that block's E8M0 byte.
+//
+// K % 128 == 0 (every hidden size in practice): 256 x 256 output tile, 8 waves (2 per SIMD) of
+// 128 x 64, K in steps of 128 (two MFMA sub-steps).  Since nothing is unpacked, operands go from
+// global memory straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at its slot
+// of a 1 KiB window), through a ring of three stage buffers, two steps ahead, with no VGPRs held
+// for the fetch.  The second sub-step's MFMAs are deferred past the LDS-only barrier that ends
+// each step, as in the NVFP4 kernel, and the epilogues are shared with it.
+// Other K (K % 32 == 0): a plainer kernel with zero-padded guarded loads through registers.
 
 #include "device_codecs.hpp"
+#include "gemm_common.hpp"
 #include "host_util.hpp"
 
 namespace nvfp4 {
 
 typedef int int8v __attribute__((ext_vector_type(8)));
-typedef float float16v_mx __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kMxBK = 128;               // K elements per pipeline step (two MFMAs)
 constexpr int kMxRowBytes = kMxBK / 2;   // 64 packed bytes per row per step
 constexpr int kFmtFp4 = 4;               // f8f6f4 operand format code for E2M1
 
-__device__ __forceinline__ void mx_tile_coords(uint32_t bid, uint32_t nbm, uint32_t nbn,
-                                               uint32_t& bm, uint32_t& bn) {
-    const uint32_t total = nbm * nbn;
-    uint32_t id = bid;
-    if ((total & 7u) == 0) id = (bid & 7u) * (total >> 3) + (bid >> 3);
-    constexpr uint32_t kGroupM = 8;
-    const uint32_t per_group = kGroupM * nbn;
-    const uint32_t g = id / per_group;
-    const uint32_t first_m = g * kGroupM;
-    const uint32_t gm = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
-    const uint32_t in = id - g * per_group;
-    bm = first_m + in % gm;
-    bn = in / gm;
+// An FP4 MFMA operand: the builtin takes eight dwords (room for FP8); E2M1 uses the first four,
+// so the rest is left undefined and the instruction reads a 4-register tuple.
+__device__ __forceinline__ int8v fp4_operand(uint4 v) {
+    const int4v w = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    return __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
-// Stage of ROWS rows: 64 code bytes (four 16-byte chunks) and 4 E8M0 bytes per row.
+// ---- K % 128 == 0: direct-to-LDS pipeline ---------------------------------------------------
+
+constexpr int kMxTile = 256;             // BM = BN
+constexpr int kMxThreads = 512;          // 8 waves
+constexpr int kMxStages = 3;             // LDS ring: the step being multiplied + two in flight
+constexpr int kMxDmaPerStep = 5;         // global->LDS loads per wave per step
+
+struct MxOperand {
+    const uint8_t* codes;    // [rows x K/2]
+    const uint8_t* scales;   // [rows x K/32] E8M0
+    int64_t rows;
+};
+
+// One step in LDS: per operand 256 rows x four 16-byte chunks (chunk c = K-block c of the step,
+// stored at slot c ^ ((r / 4) % 4), so 16 consecutive rows reading one chunk hit 16 distinct
+// bank groups) and each row's four E8M0 bytes (byte c = block c).
+struct alignas(16) MxStage {
+    uint4 a[kMxTile * 4];
+    uint4 b[kMxTile * 4];
+    uint32_t sa[kMxTile];
+    uint32_t sb[kMxTile];
+};
+static_assert(sizeof(MxStage) == 34816, "stage layout");
+
+__device__ __forceinline__ int mx_swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// global -> LDS without VGPRs: lane l's 16 (or 4) bytes from g land at LDS address lds + 16 l
+// (or 4 l); lds is wave-uniform and goes in M0.  Written as asm so that the compiler, which
+// cannot tell these writes from the ones in flight for later steps, does not wait for all of
+// them before every LDS read; completion is waited for explicitly (wait_vmcnt).  The nop is
+// the wait state gfx9 needs between writing M0 and an LDS-DMA load.
+__device__ __forceinline__ void lds_dma16(const uint8_t* g, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const uint8_t* g, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding, expcnt and lgkmcnt left at their maxima): at most n of this
+// wave's vector-memory loads still outstanding.  Loads complete in issue order.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// This lane's sources for one step.  Wave w fetches A rows [32w, 32w + 32) and the same B rows
+// (two 1 KiB windows each: 16 rows x 64 bytes, lane l -> row l / 4, slot l % 4, which holds
+// chunk (l % 4) ^ swizzle), and the scale words of 64 rows: waves 0-3 those of A, 4-7 of B.
+// Rows past the matrix are clamped to its last row (never stored); steps past the end are
+// clamped to the last step (never read), so every load is in bounds and none is conditional.
+struct MxDma {
+    const uint8_t *a0, *a1, *b0, *b1, *s;
+    int nk;
+    __device__ __forceinline__ void init(const MxOperand& A, const MxOperand& B, int64_t m0,
+                                         int64_t n0, int K, int wave, int lane) {
+        const int64_t rb = K / 2, nkb = K / 32;
+        const int rr0 = (2 * wave) * 16 + (lane >> 2), rr1 = rr0 + 16;
+        const int c0 = mx_swz(rr0, lane & 3), c1 = mx_swz(rr1, lane & 3);
+        const int64_t ma = A.rows - 1, mb = B.rows - 1;
+        a0 = A.codes + (m0 + rr0 < ma ? m0 + rr0 : ma) * rb + c0 * 16;
+        a1 = A.codes + (m0 + rr1 < ma ? m0 + rr1 : ma) * rb + c1 * 16;
+        b0 = B.codes + (n0 + rr0 < mb ? n0 + rr0 : mb) * rb + c0 * 16;
+        b1 = B.codes + (n0 + rr1 < mb ? n0 + rr1 : mb) * rb + c1 * 16;
+        const bool isb = wave >= 4;
+        const int64_t r = (isb ? n0 : m0) + (wave & 3) * 64 + lane, last = isb ? mb : ma;
+        s = (isb ? B.scales : A.scales) + (r < last ? r : last) * nkb;
+        nk = K / kMxBK;
+    }
+    // Step `step` into the stage at LDS byte address `stage` (wave-uniform).
+    __device__ __forceinline__ void issue(int step, uint32_t stage, int wave) const {
+        const int64_t k = step < nk ? step : nk - 1;
+        const uint32_t wa = stage + (2 * wave) * 1024;
+        lds_dma16(a0 + k * kMxRowBytes, wa);
+        lds_dma16(a1 + k * kMxRowBytes, wa + 1024);
+        lds_dma16(b0 + k * kMxRowBytes, wa + 16384);
+        lds_dma16(b1 + k * kMxRowBytes, wa + 16384 + 1024);
+        lds_dma4(s + k * 4, stage + 32768 + wave * 256);
+    }
+};
+
+// The operands one wave multiplies in one sub-step s (K-block q = 2s + lane / 32 of each row).
+template <int TM, int TN>
+struct MxFrags {
+    uint4 a[TM], b[TN];
+    uint32_t ea[TM], eb[TN];
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void mx_read_frags(const MxStage& st, MxFrags<TM, TN>& f, int wm, int wn,
+                                              int lane, int s) {
+    const int lrow = lane & 31, q = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * TM * 32 + i * 32 + lrow;
+        f.a[i] = st.a[r * 4 + mx_swz(r, q)];
+        f.ea[i] = (st.sa[r] >> (8 * q)) & 0xFFu;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * 32 + j * 32 + lrow;
+        f.b[j] = st.b[r * 4 + mx_swz(r, q)];
+        f.eb[j] = (st.sb[r] >> (8 * q)) & 0xFFu;
+    }
+}
+
+// kT: B is the MFMA's first operand and each accumulator tile is held transposed (the layout
+// the staged bf16 epilogue takes); otherwise one output column per lane.
+template <int TM, int TN, bool kT>
+__device__ __forceinline__ void mx_mfma(const MxFrags<TM, TN>& f, float16v (&acc)[TM][TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int8v va = fp4_operand(f.a[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int8v vb = fp4_operand(f.b[j]);
+            acc[i][j] = kT ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                 vb, va, acc[i][j], kFmtFp4, kFmtFp4, 0, (int)f.eb[j], 0, (int)f.ea[i])
+                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                 va, vb, acc[i][j], kFmtFp4, kFmtFp4, 0, (int)f.ea[i], 0, (int)f.eb[j]);
+        }
+    }
+}
+
+template <int WM, int WN, int TM, int TN, bool kBF16Out>
+__global__ void __launch_bounds__(kMxThreads)
+k_gemm_mxfp4_dma(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict__ C, int64_t ldc) {
+    static_assert(WM * WN == kMxThreads / 64 && WM * TM * 32 == kMxTile && WN * TN * 32 == kMxTile,
+                  "tile");
+    constexpr bool kT = kBF16Out;
+    // the stage ring, reused afterwards as the epilogue's staging area (16 KiB per wave)
+    constexpr int kRing = kMxStages * (int)sizeof(MxStage), kStaging = (kMxThreads / 64) * 16384;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRing > kStaging ? kRing : kStaging];
+    const MxStage* st = reinterpret_cast<const MxStage*>(lds);
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const uint32_t nbm = (M + kMxTile - 1) / kMxTile, nbn = (N + kMxTile - 1) / kMxTile;
+    uint32_t bm, bn;
+    tile_coords(blockIdx.x, nbm, nbn, bm, bn);
+    const int64_t m0 = (int64_t)bm * kMxTile, n0 = (int64_t)bn * kMxTile;
+
+    float16v acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    MxDma dma;
+    dma.init(A, B, m0, n0, K, wave, lane);
+    const int nk = dma.nk;
+    dma.issue(0, lds0, wave);
+    dma.issue(1, lds0 + sizeof(MxStage), wave);
+    MxFrags<TM, TN> f0, f1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) { f1.a[i] = make_uint4(0, 0, 0, 0); f1.ea[i] = 127; }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) { f1.b[j] = make_uint4(0, 0, 0, 0); f1.eb[j] = 127; }
+    wait_vmcnt<kMxDmaPerStep>();                        // step 0 has landed
+    lds_barrier();
+    mx_read_frags<TM, TN>(st[0], f0, wm, wn, lane, 0);
+    // Step kt multiplies stage kt % 3 while steps kt + 1 and kt + 2 are in flight; stage
+    // (kt + 2) % 3 held step kt - 1, whose last reads finished before the barrier that ended it.
+    int cs = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int ns = cs == 0 ? 2 : cs - 1;            // (kt + 2) % 3
+        dma.issue(kt + 2, lds0 + ns * (uint32_t)sizeof(MxStage), wave);
+        mx_mfma<TM, TN, kT>(f1, acc);                   // previous step, sub-step 1
+        __builtin_amdgcn_sched_barrier(0);
+        mx_read_frags<TM, TN>(st[cs], f1, wm, wn, lane, 1);
+        mx_mfma<TM, TN, kT>(f0, acc);                   // sub-step 0
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kMxDmaPerStep>();                    // step kt + 1 has landed
+        lds_barrier();
+        cs = cs == 2 ? 0 : cs + 1;
+        mx_read_frags<TM, TN>(st[cs], f0, wm, wn, lane, 0);
+    }
+    mx_mfma<TM, TN, kT>(f1, acc);                       // sub-step 1 of the last step
+    wait_vmcnt<0>();                                    // the clamped re-fetches past the end
+
+    const int64_t r0 = m0 + wm * TM * 32, c0 = n0 + wn * TN * 32;
+    if constexpr (kBF16Out) {
+        const bool vec = (reinterpret_cast<uintptr_t>(C) & 15u) == 0 && (ldc * 2) % 16 == 0;
+        __syncthreads();                    // every wave is done with the stage ring
+        epilogue_bf16<TM, TN>(acc, 1.0f, lds + wave * 16384, lane, r0, c0, M, N,
+                              reinterpret_cast<uint16_t*>(C), ldc, vec);
+    } else {
+        epilogue_f32<TM, TN>(acc, 1.0f, lane, r0, c0, M, N, reinterpret_cast<float*>(C), ldc);
+    }
+}
+
+// ---- any K % 32 == 0: guarded loads through registers ---------------------------------------
+
+// A stage of ROWS rows: 64 code bytes (four 16-byte chunks) and 4 E8M0 bytes per row.  Blocks
+// past K and rows past the matrix load as zero codes with unit scales.
 template <int ROWS, int NT>
-struct MxStage {
+struct MxRegStage {
     static constexpr int kChunks = ROWS * 4;
     static constexpr int kPerThread = (kChunks + NT - 1) / NT;
     uint4 c[kPerThread];
     uint32_t s;
-
-    // K % 128 == 0: rows past the edge clamped to the last row (their results are never stored),
-    // k0 past the end clamped to the last step by the caller, so no load is conditional and the
-    // compiler's wait counts stay exact.
-    __device__ __forceinline__ void load_fast(const uint8_t* codes, const uint8_t* scales,
-                                              int64_t rows, int64_t row0, int k0, int K, int tid) {
-        static_assert(kChunks % NT == 0 && ROWS <= NT, "fast loader shape");
-        const int64_t rb = K / 2, nkb = K / 32;
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int ch = tid + i * NT;
-            const int r = ch >> 2, q = ch & 3;
-            int64_t row = row0 + r;
-            row = row < rows - 1 ? row : rows - 1;
-            c[i] = *reinterpret_cast<const uint4*>(codes + row * rb + k0 / 2 + q * 16);
-        }
-        int64_t row = row0 + (tid < ROWS ? tid : 0);
-        row = row < rows - 1 ? row : rows - 1;
-        s = *reinterpret_cast<const uint32_t*>(scales + row * nkb + k0 / 32);
-    }
 
     __device__ __forceinline__ void load(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                          int64_t row0, int k0, int K, int tid) {
@@ -104,11 +282,11 @@ struct MxStage {
     }
 };
 
-template <int WM, int WN, int TM, int TN, bool kBF16Out, bool kFast>
+template <int WM, int WN, int TM, int TN, bool kBF16Out>
 __global__ void __launch_bounds__(WM * WN * 64)
-k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
-             const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
-             int M, int N, int K, void* __restrict__ C, int64_t ldc) {
+k_gemm_mxfp4_any(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+                 const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales,
+                 int M, int N, int K, void* __restrict__ C, int64_t ldc) {
     constexpr int NT = WM * WN * 64, BM = WM * TM * 32, BN = WN * TN * 32;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kMxRowBytes];
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kMxRowBytes];
@@ -119,10 +297,10 @@ k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_
     const int wm = wave / WN, wn = wave % WN;
     const uint32_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
     uint32_t bm, bn;
-    mx_tile_coords(blockIdx.x, nbm, nbn, bm, bn);
+    tile_coords(blockIdx.x, nbm, nbn, bm, bn);
     const int64_t m0 = (int64_t)bm * BM, n0 = (int64_t)bn * BN;
 
-    float16v_mx acc[TM][TN];
+    float16v acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -130,16 +308,11 @@ k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    MxStage<BM, NT> sa;
-    MxStage<BN, NT> sb;
+    MxRegStage<BM, NT> sa;
+    MxRegStage<BN, NT> sb;
     const int nk = (K + kMxBK - 1) / kMxBK;
-    if constexpr (kFast) {
-        sa.load_fast(a_codes, a_scales, M, m0, 0, K, tid);
-        sb.load_fast(b_codes, b_scales, N, n0, 0, K, tid);
-    } else {
-        sa.load(a_codes, a_scales, M, m0, 0, K, tid);
-        sb.load(b_codes, b_scales, N, n0, 0, K, tid);
-    }
+    sa.load(a_codes, a_scales, M, m0, 0, K, tid);
+    sb.load(b_codes, b_scales, N, n0, 0, K, tid);
     sa.store(lds_a[0], lds_sa[0], tid);
     sb.store(lds_b[0], lds_sb[0], tid);
     __syncthreads();
@@ -147,11 +320,7 @@ k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_
     const int lrow = lane & 31, h = lane >> 5;
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if constexpr (kFast) {
-            const int kn = (kt + 1 < nk ? kt + 1 : kt) * kMxBK;
-            sa.load_fast(a_codes, a_scales, M, m0, kn, K, tid);
-            sb.load_fast(b_codes, b_scales, N, n0, kn, K, tid);
-        } else if (kt + 1 < nk) {
+        if (kt + 1 < nk) {
             sa.load(a_codes, a_scales, M, m0, (kt + 1) * kMxBK, K, tid);
             sb.load(b_codes, b_scales, N, n0, (kt + 1) * kMxBK, K, tid);
         }
@@ -163,15 +332,13 @@ k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int r = wm * TM * 32 + i * 32 + lrow;
-                const uint4 v = *reinterpret_cast<const uint4*>(&lds_a[cur][r * kMxRowBytes + ((q + r) & 3) * 16]);
-                va[i] = int8v{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                va[i] = fp4_operand(*reinterpret_cast<const uint4*>(&lds_a[cur][r * kMxRowBytes + ((q + r) & 3) * 16]));
                 ea[i] = (lds_sa[cur][r] >> (8 * q)) & 0xFFu;
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int r = wn * TN * 32 + j * 32 + lrow;
-                const uint4 v = *reinterpret_cast<const uint4*>(&lds_b[cur][r * kMxRowBytes + ((q + r) & 3) * 16]);
-                vb[j] = int8v{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                vb[j] = fp4_operand(*reinterpret_cast<const uint4*>(&lds_b[cur][r * kMxRowBytes + ((q + r) & 3) * 16]));
                 eb[j] = (lds_sb[cur][r] >> (8 * q)) & 0xFFu;
             }
 #pragma unroll
@@ -181,38 +348,33 @@ k_gemm_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         va[i], vb[j], acc[i][j], kFmtFp4, kFmtFp4, 0, (int)ea[i], 0, (int)eb[j]);
         }
-        if (kFast || kt + 1 < nk) {
+        if (kt + 1 < nk) {
             sa.store(lds_a[cur ^ 1], lds_sa[cur ^ 1], tid);
             sb.store(lds_b[cur ^ 1], lds_sb[cur ^ 1], tid);
         }
-        if constexpr (kFast) {
-            // orders LDS only: the loads were all consumed by the stores above
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        } else {
-            __syncthreads();
-        }
+        __syncthreads();
     }
-
+    {
+        const int64_t r0 = m0 + wm * TM * 32, c0 = n0 + wn * TN * 32;
+        // column-per-lane accumulator layout: element r of tile (i, j) is row
+        // r0 + 32 i + 8 (r / 4) + 4 h + r % 4, column c0 + 32 j + lane % 32
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wn * TN * 32 + j * 32 + lrow;
-            if (col >= N) continue;
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = c0 + j * 32 + lrow;
+                if (col >= N) continue;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < M) {
-                    const float v = acc[i][j][r];
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = r0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (row >= M) continue;
                     if constexpr (kBF16Out)
-                        reinterpret_cast<uint16_t*>(C)[row * ldc + col] = (uint16_t)f32_to_bf16(v);
+                        reinterpret_cast<uint16_t*>(C)[row * ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
                     else
-                        reinterpret_cast<float*>(C)[row * ldc + col] = v;
+                        reinterpret_cast<float*>(C)[row * ldc + col] = acc[i][j][r];
                 }
             }
-        }
+    }
 }
 
 }  // namespace nvfp4
@@ -230,22 +392,32 @@ extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     if (s) return s;
     const int64_t M = a->rows, N = b->rows, K = a->cols;
     if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return NVFP4_ERR_SHAPE;
-    if (((M + 255) / 256) * ((N + 255) / 256) >= (1ll << 31)) return NVFP4_ERR_SHAPE;   // grid
+    if (((M + kMxTile - 1) / kMxTile) * ((N + kMxTile - 1) / kMxTile) >= (1ll << 31))
+        return NVFP4_ERR_SHAPE;
     if (M == 0 || N == 0) return NVFP4_OK;
-    constexpr int WM = 2, WN = 2, TM = 4, TN = 4;
-    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-    const uint32_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-    const dim3 grid(nbm * nbn), block(WM * WN * 64);
     hipStream_t st = as_stream(stream);
-    const bool fast = K % kMxBK == 0;
-#define NVFP4_MX(BF, FAST)                                                                        \
-    hipLaunchKernelGGL((k_gemm_mxfp4<WM, WN, TM, TN, BF, FAST>), grid, block, 0, st, a->codes,     \
-                       a->scales, b->codes, b->scales, (int)M, (int)N, (int)K, c, ldc)
-    if (c_dt == NVFP4_BF16) {
-        if (fast) NVFP4_MX(true, true); else NVFP4_MX(true, false);
-    } else {
-        if (fast) NVFP4_MX(false, true); else NVFP4_MX(false, false);
+    const bool bf16 = c_dt == NVFP4_BF16;
+    if (K == 0) {                                  // no codes to read (they may be null)
+        launch_zero_c(c, bf16, ldc, (int)M, (int)N, st);
+        return launch_status();
     }
-#undef NVFP4_MX
+    const uint32_t nbm = (M + kMxTile - 1) / kMxTile, nbn = (N + kMxTile - 1) / kMxTile;
+    const dim3 grid(nbm * nbn);
+    if (K % kMxBK == 0) {
+        const MxOperand da{a->codes, a->scales, M}, db{b->codes, b->scales, N};
+        if (bf16)
+            hipLaunchKernelGGL((k_gemm_mxfp4_dma<2, 4, 4, 2, true>), grid, dim3(kMxThreads), 0, st,
+                               da, db, (int)M, (int)N, (int)K, c, ldc);
+        else
+            hipLaunchKernelGGL((k_gemm_mxfp4_dma<2, 4, 4, 2, false>), grid, dim3(kMxThreads), 0, st,
+                               da, db, (int)M, (int)N, (int)K, c, ldc);
+    } else {
+        if (bf16)
+            hipLaunchKernelGGL((k_gemm_mxfp4_any<2, 2, 4, 4, true>), grid, dim3(256), 0, st,
+                               a->codes, a->scales, b->codes, b->scales, (int)M, (int)N, (int)K, c, ldc);
+        else
+            hipLaunchKernelGGL((k_gemm_mxfp4_any<2, 2, 4, 4, false>), grid, dim3(256), 0, st,
+                               a->codes, a->scales, b->codes, b->scales, (int)M, (int)N, (int)K, c, ldc);
+    }
     return launch_status();
 }

@@ -142,9 +142,33 @@ def test_gemm_wgrad_full(nv, orc):
 
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 64), (256, 256, 256), (100, 70, 96), (300, 520, 1056),
-                                   (300, 520, 1024), (512, 768, 2048)])
+                                   (300, 520, 1024), (512, 768, 2048), (40, 600, 128),
+                                   (1000, 300, 384), (257, 513, 640)])
 def test_mx_gemm(nv, orc, M, N, K):
+    """K % 128 == 0 takes the direct-to-LDS pipeline (one, two, three, five and more K steps;
+    ragged M and N), other K the guarded kernel."""
     a = W.act((M, K), 51)
     b = W.act((N, K), 52)
     qa, qb = nv.mx_quantize_1d(a.to(DEV)), nv.mx_quantize_1d(b.to(DEV))
     _check_gemm(nv, orc, qa, qb, mx=True)
+
+
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gemm_empty_k(nv, mx, dtype):
+    """K == 0: every output is an empty sum, so the whole (strided) window of C becomes 0 and
+    nothing around it changes; the operands' code and scale pointers are null and never read."""
+    M, N = 300, 520
+    layout = nv.MX_1x32 if mx else nv.BLK_1x16
+    qa, qb = nv.QTensor.empty(M, 0, layout, DEV), nv.QTensor.empty(N, 0, layout, DEV)
+    assert qa.codes.data_ptr() == 0 and qb.scales.data_ptr() == 0
+    if not mx:
+        qa.s_dec.fill_(1.0)
+        qb.s_dec.fill_(1.0)
+    big = torch.full((M, N + 40), 7.0, dtype=dtype, device=DEV)
+    out = big[:, 8:8 + N]
+    (nv.mx_gemm if mx else nv.gemm)(qa, qb, dtype, out=out)
+    torch.cuda.synchronize()
+    host = big.cpu().float()
+    assert torch.all(host[:, 8:8 + N] == 0)
+    assert torch.all(host[:, :8] == 7) and torch.all(host[:, 8 + N:] == 7)
