@@ -143,7 +143,8 @@ def test_gemm_wgrad_full(nv, orc):
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 64), (256, 256, 256), (100, 70, 96), (300, 520, 1056),
                                    (300, 520, 1024), (512, 768, 2048), (40, 600, 128),
-                                   (1000, 300, 384), (257, 513, 640)])
+                                   (1000, 300, 384), (257, 513, 640), (1, 1, 128), (1, 700, 256),
+                                   (530, 1, 384)])
 def test_mx_gemm(nv, orc, M, N, K):
     """K % 128 == 0 takes the direct-to-LDS pipeline (one, two, three, five and more K steps;
     ragged M and N), other K the guarded kernel."""
