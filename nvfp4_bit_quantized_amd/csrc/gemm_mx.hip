@@ -9,7 +9,7 @@
 // One MFMA covers K = 64: lane l supplies row l%32 and the 32-element block (l/32) of the 64,
 // i.e. 16 bytes of codes plus that block's E8M0 byte.
 //
-// K % 128 == 0 (every hidden size in practice): 256 x 256 output tile, 8 waves (2 per SIMD) of
+// K % 128 == 0 (all the step and FFN-pair shapes): 256 x 256 output tile, 8 waves (2 per SIMD) of
 // 128 x 64, K in steps of 128 (two MFMA sub-steps).  Since nothing is unpacked, operands go from
 // global memory straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at its slot
 // of a 1 KiB window), through a ring of three stage buffers, two steps ahead, with no VGPRs held
