@@ -9,12 +9,16 @@
 // One MFMA covers K = 64: lane l supplies row l%32 and the 32-element block (l/32) of the 64,
 // i.e. 16 bytes of codes plus that block's E8M0 byte.
 //
-// K % 128 == 0 (all the step and FFN-pair shapes): 256 x 256 output tile, 8 waves (2 per SIMD) of
-// 128 x 64, K in steps of 128 (two MFMA sub-steps).  Since nothing is unpacked, operands go from
-// global memory straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at its slot
-// of a 1 KiB window), through a ring of three stage buffers, two steps ahead, with no VGPRs held
-// for the fetch.  The second sub-step's MFMAs are deferred past the LDS-only barrier that ends
-// each step, as in the NVFP4 kernel, and the epilogues are shared with it.
+// K % 128 == 0: 256 x 256 output tile, 8 waves (2 per SIMD) of 128 x 64.  Since nothing is
+// unpacked, operands go from global memory straight into LDS (global_load_lds_dwordx4: each
+// lane's 16 bytes land at its slot of a 1 KiB window), with no VGPRs held for the fetch.  The
+// last sub-step's MFMAs are deferred past the LDS-only barrier that ends each step, as in the
+// NVFP4 kernel, and the epilogues are shared with it.
+//   K % 256 == 0 (all the step and FFN-pair shapes): steps of 256 (four MFMA sub-steps) through
+//     two 68 KiB stages, one step ahead -- one barrier per 32 MFMAs per wave;
+//   otherwise steps of 128 (two sub-steps) through a ring of three 34 KiB stages, two ahead.
+// The longer step is what pays: at 128 the waves spent a third of their cycles waiting at the
+// per-step barrier and counters with the MFMA pipe 30-37% busy.
 // Other K (K % 32 == 0): a plainer kernel with zero-padded guarded loads through registers.
 
 #include "device_codecs.hpp"
@@ -37,7 +41,7 @@ __device__ __forceinline__ int8v fp4_operand(uint4 v) {
     return __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
-// ---- K % 128 == 0: direct-to-LDS pipeline ---------------------------------------------------
+// ---- K % 128 == 0: direct-to-LDS loads; steps of 128 through a three-stage ring --------------
 
 constexpr int kMxTile = 256;             // BM = BN
 constexpr int kMxThreads = 512;          // 8 waves
@@ -231,6 +235,153 @@ k_gemm_mxfp4_dma(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict
     }
 }
 
+// ---- K % 256 == 0: steps of 256 through two stages ------------------------------------------
+constexpr int kD2BK = 256, kD2RowBytes = 128;
+
+// One step in LDS: per operand 256 rows x eight 16-byte chunks (chunk c = K-block c of the step,
+// at slot c ^ ((r / 2) % 8): 16 consecutive rows reading one chunk hit 16 distinct bank groups),
+// then each row's eight E8M0 bytes as two words (blocks 0-3, 4-7).
+struct alignas(16) MxStage2 {
+    uint4 a[kMxTile * 8];
+    uint4 b[kMxTile * 8];
+    uint32_t sa[2][kMxTile];     // a row's scale bytes of blocks 0-3 and 4-7 of the step
+    uint32_t sb[2][kMxTile];
+};
+static_assert(sizeof(MxStage2) == 69632, "stage2");
+__device__ __forceinline__ int d2_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// This lane's sources for one step.  Wave w fetches A rows [32w, 32w + 32) and the same B rows
+// as four 1 KiB windows each (8 rows x 128 bytes; lane l -> row l / 8, slot l % 8), and two of
+// the sixteen 256-byte scale windows (64 rows' words of A blocks 0-3, A 4-7, B 0-3, B 4-7).  Rows
+// past the matrix and steps past K are clamped as in MxDma.  10 loads per wave per step.
+struct MxDma2 {
+    const uint8_t *a[4], *b[4], *s0, *s1;
+    int nk;
+    __device__ __forceinline__ void init(const MxOperand& A, const MxOperand& B, int64_t m0,
+                                         int64_t n0, int K, int wave, int lane) {
+        const int64_t rb = K / 2, nkb = K / 32;
+        const int64_t ma = A.rows - 1, mb = B.rows - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = (4 * wave + j) * 8 + (lane >> 3);
+            const int c = d2_swz(rr, lane & 7);
+            a[j] = A.codes + (m0 + rr < ma ? m0 + rr : ma) * rb + c * 16;
+            b[j] = B.codes + (n0 + rr < mb ? n0 + rr : mb) * rb + c * 16;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int v = 2 * wave + u;                        // 256-byte window of the scales
+            const bool isb = v >= 8;
+            const int half = (v >> 2) & 1;
+            const int64_t r = (isb ? n0 : m0) + (v & 3) * 64 + lane, last = isb ? mb : ma;
+            const uint8_t* p = (isb ? B.scales : A.scales) + (r < last ? r : last) * nkb + half * 4;
+            if (u == 0) s0 = p; else s1 = p;
+        }
+        nk = K / kD2BK;
+    }
+    __device__ __forceinline__ void issue(int step, uint32_t stage, int wave) const {
+        const int64_t k = step < nk ? step : nk - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lds_dma16(a[j] + k * kD2RowBytes, stage + (4 * wave + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lds_dma16(b[j] + k * kD2RowBytes, stage + 32768 + (4 * wave + j) * 1024);
+        lds_dma4(s0 + k * 8, stage + 65536 + (2 * wave) * 256);
+        lds_dma4(s1 + k * 8, stage + 65536 + (2 * wave + 1) * 256);
+    }
+};
+
+// The fragments of sub-step s (K-block q = 2s + lane / 32 of each row).
+template <int TM, int TN>
+__device__ __forceinline__ void d2_read_frags(const MxStage2& st, MxFrags<TM, TN>& f, int wm, int wn,
+                                              int lane, int s) {
+    const int lrow = lane & 31, q = 2 * s + (lane >> 5), sh = 8 * (q & 3), wsel = s >> 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * TM * 32 + i * 32 + lrow;
+        f.a[i] = st.a[r * 8 + d2_swz(r, q)];
+        f.ea[i] = (st.sa[wsel][r] >> sh) & 0xFFu;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * 32 + j * 32 + lrow;
+        f.b[j] = st.b[r * 8 + d2_swz(r, q)];
+        f.eb[j] = (st.sb[wsel][r] >> sh) & 0xFFu;
+    }
+}
+
+template <int WM, int WN, int TM, int TN, bool kBF16Out>
+__global__ void __launch_bounds__(kMxThreads)
+k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict__ C, int64_t ldc) {
+    constexpr bool kT = kBF16Out;
+    constexpr int kRing = 2 * (int)sizeof(MxStage2), kStaging = (kMxThreads / 64) * 16384;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRing > kStaging ? kRing : kStaging];
+    const MxStage2* st = reinterpret_cast<const MxStage2*>(lds);
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(lds);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const uint32_t nbm = (M + kMxTile - 1) / kMxTile, nbn = (N + kMxTile - 1) / kMxTile;
+    uint32_t bm, bn;
+    tile_coords(blockIdx.x, nbm, nbn, bm, bn);
+    const int64_t m0 = (int64_t)bm * kMxTile, n0 = (int64_t)bn * kMxTile;
+
+    float16v acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    MxDma2 dma;
+    dma.init(A, B, m0, n0, K, wave, lane);
+    const int nk = dma.nk;
+    dma.issue(0, lds0, wave);
+    MxFrags<TM, TN> f0, f1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) { f1.a[i] = make_uint4(0, 0, 0, 0); f1.ea[i] = 127; }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) { f1.b[j] = make_uint4(0, 0, 0, 0); f1.eb[j] = 127; }
+    wait_vmcnt<0>();
+    lds_barrier();
+    dma.issue(1, lds0 + sizeof(MxStage2), wave);
+    d2_read_frags<TM, TN>(st[0], f0, wm, wn, lane, 0);
+    // Step kt multiplies stage kt % 2 while step kt + 1 lands in the other; after the barrier
+    // that ends step kt (all reads of its stage done) step kt + 2 is fetched into it.
+    int cs = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const MxStage2& cur = st[cs];
+        mx_mfma<TM, TN, kT>(f1, acc);                   // previous step, sub-step 3
+        __builtin_amdgcn_sched_barrier(0);
+        d2_read_frags<TM, TN>(cur, f1, wm, wn, lane, 1);
+        mx_mfma<TM, TN, kT>(f0, acc);                   // sub-step 0
+        __builtin_amdgcn_sched_barrier(0);
+        d2_read_frags<TM, TN>(cur, f0, wm, wn, lane, 2);
+        mx_mfma<TM, TN, kT>(f1, acc);                   // sub-step 1
+        __builtin_amdgcn_sched_barrier(0);
+        d2_read_frags<TM, TN>(cur, f1, wm, wn, lane, 3);
+        mx_mfma<TM, TN, kT>(f0, acc);                   // sub-step 2
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<0>();                                // step kt + 1 has landed
+        lds_barrier();
+        dma.issue(kt + 2, lds0 + cs * (uint32_t)sizeof(MxStage2), wave);
+        cs ^= 1;
+        d2_read_frags<TM, TN>(st[cs], f0, wm, wn, lane, 0);
+    }
+    mx_mfma<TM, TN, kT>(f1, acc);                       // sub-step 3 of the last step
+    wait_vmcnt<0>();                                    // the clamped re-fetches past the end
+
+    const int64_t r0 = m0 + wm * TM * 32, c0 = n0 + wn * TN * 32;
+    if constexpr (kBF16Out) {
+        const bool vec = (reinterpret_cast<uintptr_t>(C) & 15u) == 0 && (ldc * 2) % 16 == 0;
+        __syncthreads();                    // every wave is done with the stages
+        epilogue_bf16<TM, TN>(acc, 1.0f, lds + wave * 16384, lane, r0, c0, M, N,
+                              reinterpret_cast<uint16_t*>(C), ldc, vec);
+    } else {
+        epilogue_f32<TM, TN>(acc, 1.0f, lane, r0, c0, M, N, reinterpret_cast<float*>(C), ldc);
+    }
+}
+
 // ---- any K % 32 == 0: guarded loads through registers ---------------------------------------
 
 // A stage of ROWS rows: 64 code bytes (four 16-byte chunks) and 4 E8M0 bytes per row.  Blocks
@@ -403,7 +554,15 @@ extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     }
     const uint32_t nbm = (M + kMxTile - 1) / kMxTile, nbn = (N + kMxTile - 1) / kMxTile;
     const dim3 grid(nbm * nbn);
-    if (K % kMxBK == 0) {
+    if (K % kD2BK == 0) {
+        const MxOperand da{a->codes, a->scales, M}, db{b->codes, b->scales, N};
+        if (bf16)
+            hipLaunchKernelGGL((k_gemm_mxfp4_d2<2, 4, 4, 2, true>), grid, dim3(kMxThreads), 0, st,
+                               da, db, (int)M, (int)N, (int)K, c, ldc);
+        else
+            hipLaunchKernelGGL((k_gemm_mxfp4_d2<2, 4, 4, 2, false>), grid, dim3(kMxThreads), 0, st,
+                               da, db, (int)M, (int)N, (int)K, c, ldc);
+    } else if (K % kMxBK == 0) {
         const MxOperand da{a->codes, a->scales, M}, db{b->codes, b->scales, N};
         if (bf16)
             hipLaunchKernelGGL((k_gemm_mxfp4_dma<2, 4, 4, 2, true>), grid, dim3(kMxThreads), 0, st,

@@ -144,10 +144,11 @@ def test_gemm_wgrad_full(nv, orc):
 @pytest.mark.parametrize("M,N,K", [(32, 32, 64), (256, 256, 256), (100, 70, 96), (300, 520, 1056),
                                    (300, 520, 1024), (512, 768, 2048), (40, 600, 128),
                                    (1000, 300, 384), (257, 513, 640), (1, 1, 128), (1, 700, 256),
-                                   (530, 1, 384)])
+                                   (530, 1, 384), (777, 1000, 768)])
 def test_mx_gemm(nv, orc, M, N, K):
-    """K % 128 == 0 takes the direct-to-LDS pipeline (one, two, three, five and more K steps;
-    ragged M and N), other K the guarded kernel."""
+    """K % 256 == 0 takes the two-stage direct-to-LDS kernel (one, three, four and eight K steps),
+    other K % 128 == 0 the three-stage one (one, three and five steps), both with ragged M and N;
+    other K the guarded kernel."""
     a = W.act((M, K), 51)
     b = W.act((N, K), 52)
     qa, qb = nv.mx_quantize_1d(a.to(DEV)), nv.mx_quantize_1d(b.to(DEV))
