@@ -234,8 +234,9 @@ __global__ void k_fill_f64x2(double* p) {
 // ---- 2D quantization of weights [P1 Metodologia: two-dimensional block scaling] ---------------
 // A wave covers kQ2Groups groups of 4 tiles of 16x16; in each group lane (t = lane/16,
 // r = lane%16) holds row r of tile t (16 elements).  All of a lane's loads are issued before any
-// arithmetic.  One group per wave measured fastest (four: 20 us instead of 18 on 4096^2 bf16).  The tile amax is a max over the 16 lanes of the tile.  The transposed copy is
-// built by staging each tile's codes in LDS, one byte per element.
+// arithmetic.  One group per wave measured fastest (four: 20 us instead of 18 on 4096^2 bf16).
+// The tile amax is a max over the 16 lanes of the tile.  The transposed copy is built by staging
+// each tile's codes in LDS, one byte per element.
 constexpr int kQ2Groups = 1;
 
 template <typename T>
