@@ -414,7 +414,8 @@ struct MxRegStage {
                 const int kb0 = k0 / 32;
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    if (kb0 + b < nkb) s = (s & ~(0xFFu << (8 * b))) | ((uint32_t)scales[row * nkb + kb0 + b] << (8 * b));
+                    if (kb0 + b < nkb)
+                        s = (s & ~(0xFFu << (8 * b))) | ((uint32_t)scales[row * nkb + kb0 + b] << (8 * b));
             }
         }
     }
@@ -483,13 +484,15 @@ k_gemm_mxfp4_any(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict_
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int r = wm * TM * 32 + i * 32 + lrow;
-                va[i] = fp4_operand(*reinterpret_cast<const uint4*>(&lds_a[cur][r * kMxRowBytes + ((q + r) & 3) * 16]));
+                const uint8_t* p = &lds_a[cur][r * kMxRowBytes + ((q + r) & 3) * 16];
+                va[i] = fp4_operand(*reinterpret_cast<const uint4*>(p));
                 ea[i] = (lds_sa[cur][r] >> (8 * q)) & 0xFFu;
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int r = wn * TN * 32 + j * 32 + lrow;
-                vb[j] = fp4_operand(*reinterpret_cast<const uint4*>(&lds_b[cur][r * kMxRowBytes + ((q + r) & 3) * 16]));
+                const uint8_t* p = &lds_b[cur][r * kMxRowBytes + ((q + r) & 3) * 16];
+                vb[j] = fp4_operand(*reinterpret_cast<const uint4*>(p));
                 eb[j] = (lds_sb[cur][r] >> (8 * q)) & 0xFFu;
             }
 #pragma unroll
