@@ -76,39 +76,6 @@ __device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts
 
 // ---- E2M1 [P1 Caracteristicas: 1 sign, 2 exponent, 1 mantissa bit] --------------------------
 
-// Stochastic rounding of one element [P2 Describir: stochastic rounding in the backward pass]:
-// with lo <= |z| < hi the neighbouring grid values, round up iff r16 < 65536 (|z|-lo)/(hi-lo);
-// |z| >= 6 saturates; sign kept.  Works on z2 = 2z (callers form it as z + z, exact) whose grid
-// 0,1,2,3,4,6,8,12 has spacing 1 below 4, 2 in [4,8) and 4 above: scaling a2 = |z2| by 2^-k with
-// k = 0, 1, 2 for those regions (k + 2 = the binary exponent of a2 clamped to [2, 4]) puts every
-// region on an integer grid, so (|z|-lo)/(hi-lo) = fract(a2 2^-k) and the rounded value is
-// floor(a2 2^-k) + up, all exact in fp32.  The magnitude code is that integer plus 2k, clamped
-// to 7 (which also saturates a2 >= 12).
-__device__ __forceinline__ uint32_t e2m1_sr_code2(float z2, uint32_t r16) {
-    const uint32_t zb = __float_as_uint(z2);
-    const float a = __builtin_fabsf(z2);
-    const int e = __builtin_amdgcn_frexp_expf(a);            // a = m 2^e, m in [0.5, 1)
-    const int k2 = e < 2 ? 2 : (e > 4 ? 4 : e);              // k + 2
-    const float as = __builtin_amdgcn_ldexpf(a, 2 - k2);
-    const uint32_t fl = (uint32_t)as;                        // floor: as >= 0
-    const float f = __builtin_amdgcn_fractf(as);
-    const uint32_t up = (float)r16 < f * 65536.0f;
-    const uint32_t idx = fl + up + 2u * (uint32_t)(k2 - 2);
-    return ((zb >> 28) & 8u) | (idx < 7u ? idx : 7u);
-}
-
-// Eight codes: element e takes the 16-bit half (e & 1) of w[e >> 1] (low half first), packed
-// element 2j -> low nibble of byte j.  z2[e] = 2 z[e].
-__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float* z2, const uint32_t* w) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t r16 = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
-        packed |= e2m1_sr_code2(z2[e], r16) << (4 * e);
-    }
-    return packed;
-}
-
 // Eight E2M1 codes of z[0..7] rounded to nearest even (ties to the even code, saturating at 6,
 // sign kept), packed element 2j -> low nibble of byte j.  gfx950's v_cvt_scalef32_pk_fp4_f32
 // with a unit scale performs exactly this rounding for every finite fp32 input.
@@ -119,6 +86,38 @@ __device__ __forceinline__ uint32_t e2m1_rne_pack8(const float* z) {
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[4], z[5], 1.0f, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[6], z[7], 1.0f, 3);
     return w;
+}
+
+// Stochastic rounding of one element [P2 Describir: stochastic rounding in the backward pass]:
+// with lo <= |z| < hi the neighbouring grid values, round up iff r16 < 65536 (|z|-lo)/(hi-lo);
+// |z| >= 6 saturates; sign kept.  Below 8 the E2M1 grid is uniform within three regions: spacing
+// h = 1/2 on [0, 2), 1 on [2, 4) and 2 on [4, 8), i.e. h = 2^(k-2) with k the binary exponent of
+// |z| (frexp convention) clamped to [1, 3].  With y = |z| / h (exact) and u = r16 / 65536,
+// ceil(y - u) = floor(y) + [fract(y) > u], which is the rounded value divided by h.  One fma
+// forms y - u: it is exact whenever y >= 1 (y and u lie on a common grid fine enough for 24
+// bits), and for y < 1 its single rounding cannot move the value across 0 or below u - 1, so the
+// ceiling is unchanged (checked against the definition on 2.2e8 cases, every boundary included).
+// The result h * ceil(y - u) lies on the E2M1 grid, or is 8 when |z| >= 6 rounds up, which the
+// round-to-nearest encode then saturates to 6.  A ceiling of -0 takes z's sign like any zero.
+__device__ __forceinline__ float e2m1_sr_value(float z, uint32_t r16) {
+    const float a = __builtin_fabsf(z);
+    const int e = __builtin_amdgcn_frexp_expf(a);            // a = m 2^e, m in [0.5, 1)
+    const int k = e < 1 ? 1 : (e > 3 ? 3 : e);
+    const float y = __builtin_amdgcn_ldexpf(a, 2 - k);
+    const float q = __builtin_ceilf(__builtin_fmaf((float)r16, -0x1p-16f, y));
+    return __builtin_copysignf(__builtin_amdgcn_ldexpf(q, k - 2), z);
+}
+
+// Eight stochastically rounded codes of z[0..7]: element e takes the 16-bit half (e & 1) of
+// w[e >> 1] (low half first); packed element 2j -> low nibble of byte j.
+__device__ __forceinline__ uint32_t e2m1_sr_pack8(const float* z, const uint32_t* w) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t r16 = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+        v[e] = e2m1_sr_value(z[e], r16);
+    }
+    return e2m1_rne_pack8(v);    // exact: every v is a grid value (or >= 8, saturated)
 }
 
 // ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) --------------------------------------

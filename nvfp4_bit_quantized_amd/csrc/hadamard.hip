@@ -271,23 +271,17 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
         uint32_t sb;
         float enc;
         block_scale(m, ts, sb, enc);
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = v[e] * enc;
         uint32_t lo = 0, hi = 0;
         if constexpr (kSR) {
             const uint64_t idx = (uint64_t)feat * (uint64_t)Tn + (uint64_t)rc.c * 16;
             const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
             const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
-            float z[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float ze = v[e] * enc;
-                z[e] = ze + ze;
-            }
             lo = e2m1_sr_pack8(z, a);
             hi = e2m1_sr_pack8(z + 8, b);
         } else {
-            float z[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) z[e] = v[e] * enc;
             lo = e2m1_rne_pack8(z);
             hi = e2m1_rne_pack8(z + 8);
         }
@@ -322,21 +316,15 @@ __device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const R
         float enc;
         block_scale(m, ts, sb, enc);
         const int64_t row = rc.c * 16 + i;
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = y[e] * enc;
         uint32_t packed;
         if constexpr (kSR) {
             const u32x4 w = sr_words(seed, (uint64_t)row * (uint64_t)F + (uint64_t)rc.f0);
             const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-            float z[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ze = y[e] * enc;
-                z[e] = ze + ze;
-            }
             packed = e2m1_sr_pack8(z, words);
         } else {
-            float z[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) z[e] = y[e] * enc;
             packed = e2m1_rne_pack8(z);
         }
         *reinterpret_cast<uint32_t*>(codes + row * (F / 2) + rc.f0 / 2) = packed;
@@ -421,23 +409,17 @@ k_mx_quant_t(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
             e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
             e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
         }
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = __builtin_amdgcn_ldexpf(v[e], -e8);
         uint32_t lo, hi;
         if constexpr (kSR) {
             const uint64_t idx = (uint64_t)feat * (uint64_t)Tn + (uint64_t)rc.c * 16;
             const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
             const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
-            float z[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float ze = __builtin_amdgcn_ldexpf(v[e], -e8);
-                z[e] = ze + ze;
-            }
             lo = e2m1_sr_pack8(z, a);
             hi = e2m1_sr_pack8(z + 8, b);
         } else {
-            float z[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) z[e] = __builtin_amdgcn_ldexpf(v[e], -e8);
             lo = e2m1_rne_pack8(z);
             hi = e2m1_rne_pack8(z + 8);
         }

@@ -159,23 +159,17 @@ k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uin
         uint32_t sb;
         float enc;
         block_scale(m, ts, sb, enc);
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = y[u][e] * enc;
         uint32_t lo = 0, hi = 0;
         if constexpr (kSR) {
             const uint64_t idx = (uint64_t)row[u] * cols + cb[u] * 16;
             const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
             const uint32_t wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
-            float z[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float ze = y[u][e] * enc;
-                z[e] = ze + ze;
-            }
             lo = e2m1_sr_pack8(z, wa);
             hi = e2m1_sr_pack8(z + 8, wb);
         } else {
-            float z[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) z[e] = y[u][e] * enc;
             lo = e2m1_rne_pack8(z);
             hi = e2m1_rne_pack8(z + 8);
         }
@@ -232,22 +226,53 @@ __global__ void k_fill_f64x2(double* p) {
 }
 
 // ---- 2D quantization of weights [P1 Metodologia: two-dimensional block scaling] ---------------
-// A wave covers kQ2Groups groups of 4 tiles of 16x16; in each group lane (t = lane/16,
-// r = lane%16) holds row r of tile t (16 elements).  All of a lane's loads are issued before any
-// arithmetic.  One group per wave measured fastest (four: 20 us instead of 18 on 4096^2 bf16).
-// The tile amax is a max over the 16 lanes of the tile.  The transposed copy is built by staging
-// each tile's codes in LDS, one byte per element.
-constexpr int kQ2Groups = 1;
+// A workgroup quantizes a 128 x 128 region (8 x 8 tiles of 16 x 16).  Wave v takes rows
+// [32v, 32v + 32) of the region; lane l owns the 8 x 8 block at column chunk c = l & 15 and row
+// group g = l >> 4 (rows 8g .. 8g + 7 of the wave's 32).  Its eight row loads (16 bytes each for
+// bf16) are issued before any arithmetic, and each load instruction of the wave reads four whole
+// 256-byte row segments.  A 16 x 16 tile is held by lanes l, l ^ 1, l ^ 16 and l ^ 17, so its
+// amax takes two lane exchanges.  The row-wise codes leave as one 4-byte word per block row (16
+// lanes write a region row's 64 contiguous bytes).  For the transposed copy each lane transposes
+// its 8 x 8 codes in registers (nibble_transpose8) and stages the eight column words in LDS;
+// after one barrier 16 consecutive threads write each transposed row's 64 contiguous bytes.
+// rows and cols are multiples of 16, so every 8 x 8 block (and tile) is wholly inside or outside
+// the matrix; blocks outside load a clamped, valid block and store nothing.
+constexpr int kQ2Region = 128;
+
+// In-register transpose of an 8 x 8 matrix of nibbles: on entry nibble j of w[i] is element
+// (i, j), on exit nibble i of w[j] is element (i, j).  Three exchange stages: 4 x 4 quadrants
+// (16-bit halves), 2 x 2 blocks of bytes, then single nibbles.
+__device__ __forceinline__ void nibble_transpose8(uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t a = w[i], b = w[i + 4];
+        w[i] = (a & 0x0000FFFFu) | (b << 16);
+        w[i + 4] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = (q & 1) + 4 * (q >> 1);       // 0, 1, 4, 5
+        const uint32_t a = w[i], b = w[i + 2];
+        w[i] = (a & 0x00FF00FFu) | ((b & 0x00FF00FFu) << 8);
+        w[i + 2] = ((a >> 8) & 0x00FF00FFu) | (b & 0xFF00FF00u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const uint32_t a = w[i], b = w[i + 1];
+        w[i] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+        w[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+    }
+}
 
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols, uint32_t tiles,
-          FastDiv tiles_per_row, const float* __restrict__ amax_src,
-          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-          uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
-          float* amax_out, float* sdec_out, float* amax_out_t, float* sdec_out_t) {
-    // [wave][group][tile][row][16 code bytes + 4 bytes of padding]
-    __shared__ uint32_t stage[kThreads / 64][kQ2Groups][4][16][5];
+k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols,
+          const float* __restrict__ amax_src, uint8_t* __restrict__ codes,
+          uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
+          uint8_t* __restrict__ scales_t, float* amax_out, float* sdec_out, float* amax_out_t,
+          float* sdec_out_t, uint32_t regions_per_row) {
+    // [region column][8-row group] code words of the transposed copy; one word of padding per row
+    __shared__ uint32_t stage[kQ2Region][kQ2Region / 8 + 1];
     const float A = *amax_src;
     const TensorScales ts = tensor_scales(A);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -257,72 +282,56 @@ k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols, uin
         if (sdec_out_t) *sdec_out_t = ts.s_dec;
     }
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int t = lane >> 4, r = lane & 15;
-    float y[kQ2Groups][16];
-    uint32_t ti[kQ2Groups], tj[kQ2Groups];
-    bool valid[kQ2Groups];
+    const int c = lane & 15, g = lane >> 4;
+    const int rg = wv * 4 + g;                                   // 8-row group within the region
+    const uint32_t by = blockIdx.x / regions_per_row, bx = blockIdx.x - by * regions_per_row;
+    const uint32_t row0 = by * kQ2Region, col0 = bx * kQ2Region;
+    const uint32_t r0 = row0 + rg * 8, c0 = col0 + c * 8;
+    const bool valid = r0 < rows && c0 < cols;
+    const T* src = w + (int64_t)(valid ? r0 : 0) * ld + (valid ? c0 : 0);
+    float y[8][8];
 #pragma unroll
-    for (int g = 0; g < kQ2Groups; ++g) {
-        const uint32_t tile = ((blockIdx.x * (kThreads / 64) + wv) * kQ2Groups + g) * 4 + t;
-        valid[g] = tile < tiles;
-        ti[g] = 0; tj[g] = 0;
-        if (valid[g]) {
-            ti[g] = fastdiv(tile, tiles_per_row);
-            tj[g] = tile - ti[g] * tiles_per_row.d;
-            const T* p = w + (int64_t)(ti[g] * 16 + r) * ld + tj[g] * 16;
-            Group8<T>::load(p, y[g]);
-            Group8<T>::load(p + 8, y[g] + 8);
-        } else {
+    for (int i = 0; i < 8; ++i) Group8<T>::load(src + i * ld, y[i]);
+    float m = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) y[g][e] = 0.0f;
-        }
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[i][e]));
+    m = fmaxf(m, swap_adjacent(m));                  // lane ^ 1: the tile's other column chunk
+    m = fmaxf(m, __shfl_xor(m, 16));                 // lane ^ 16: the tile's other row group
+    uint32_t sb;
+    float enc;
+    block_scale(m, ts, sb, enc);
+    uint32_t wd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = y[i][e] * enc;
+        wd[i] = e2m1_rne_pack8(z);
     }
-    uint32_t sbs[kQ2Groups];
+    if (valid) {
+        uint8_t* dst = codes + (int64_t)r0 * (cols / 2) + c0 / 2;
 #pragma unroll
-    for (int g = 0; g < kQ2Groups; ++g) {
-        float m = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(y[g][e]));
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-        uint32_t sb;
-        float enc;
-        block_scale(m, ts, sb, enc);
-        sbs[g] = sb;
-        float z[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) z[e] = y[g][e] * enc;
-        const uint32_t lo = e2m1_rne_pack8(z), hi = e2m1_rne_pack8(z + 8);
-        // one code per byte for the transposed copy
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t wd = q < 2 ? lo : hi, sh = 16 * (q & 1);
-            const uint32_t n = (wd >> sh) & 0xFFFFu;             // codes 4q .. 4q+3
-            stage[wv][g][t][r][q] = (n & 0xFu) | ((n & 0xF0u) << 4) | ((n & 0xF00u) << 8) |
-                                    ((n & 0xF000u) << 12);
-        }
-        if (valid[g]) {
-            *reinterpret_cast<uint2*>(codes + (int64_t)(ti[g] * 16 + r) * (cols / 2) + tj[g] * 8) =
-                make_uint2(lo, hi);
-            if (r == 0) scales[(int64_t)ti[g] * tiles_per_row.d + tj[g]] = (uint8_t)sb;
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(dst + (int64_t)i * (cols / 2)) = wd[i];
+        if ((lane & 0x11) == 0) {                    // one lane per tile writes its scale byte(s)
+            scales[(int64_t)(r0 / 16) * (cols / 16) + c0 / 16] = (uint8_t)sb;
+            if (scales_t) scales_t[(int64_t)(c0 / 16) * (rows / 16) + r0 / 16] = (uint8_t)sb;
         }
     }
     if (!codes_t) return;
+    nibble_transpose8(wd);                           // wd[j]: column c0 + j, rows r0 .. r0 + 7
+#pragma unroll
+    for (int j = 0; j < 8; ++j) stage[c * 8 + j][rg] = wd[j];
     __syncthreads();
+    // transposed row (col0 + tc) of [cols x rows]: 16 words for the region's 128 rows
 #pragma unroll
-    for (int g = 0; g < kQ2Groups; ++g) {
-        if (!valid[g]) continue;
-        // column r of the tile becomes row (16 tj + r) of the transposed matrix
-        const uint8_t* st = reinterpret_cast<const uint8_t*>(&stage[wv][g][t][0][0]);
-        uint32_t tlo = 0, thi = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            tlo |= (uint32_t)st[e * 20 + r] << (4 * e);
-            thi |= (uint32_t)st[(e + 8) * 20 + r] << (4 * e);
-        }
-        *reinterpret_cast<uint2*>(codes_t + (int64_t)(tj[g] * 16 + r) * (rows / 2) + ti[g] * 8) =
-            make_uint2(tlo, thi);
-        if (r == 0) scales_t[(int64_t)tj[g] * (rows / 16) + ti[g]] = (uint8_t)sbs[g];
+    for (int p = 0; p < kQ2Region * 16 / kThreads; ++p) {
+        const int idx = p * kThreads + threadIdx.x;
+        const int tc = idx >> 4, trg = idx & 15;
+        if (col0 + tc < cols && row0 + trg * 8 < rows)
+            *reinterpret_cast<uint32_t*>(codes_t + (int64_t)(col0 + tc) * (rows / 2) + row0 / 2 +
+                                         trg * 4) = stage[tc][trg];
     }
 }
 
@@ -409,22 +418,16 @@ k_mx_quant(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, ui
             e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
             e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
         }
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = __builtin_amdgcn_ldexpf(y[u][e], -e8);
         uint32_t packed = 0;
         if constexpr (kSR) {
             const uint64_t idx8 = (uint64_t)row[u] * cols + cg[u] * 8;
             const u32x4 w = sr_words(seed, idx8);
             const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-            float z[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ze = __builtin_amdgcn_ldexpf(y[u][e], -e8);
-                z[e] = ze + ze;
-            }
             packed = e2m1_sr_pack8(z, words);
         } else {
-            float z[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) z[e] = __builtin_amdgcn_ldexpf(y[u][e], -e8);
             packed = e2m1_rne_pack8(z);
         }
         if (g < groups) {
@@ -475,10 +478,8 @@ k_qdq(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uint32_
         for (int g = 0; g < B / 8; ++g) {
             float z[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ze = kE8M0 ? __builtin_amdgcn_ldexpf(v[8 * g + e], -e8) : v[8 * g + e] * enc;
-                z[e] = kSR ? ze + ze : ze;
-            }
+            for (int e = 0; e < 8; ++e)
+                z[e] = kE8M0 ? __builtin_amdgcn_ldexpf(v[8 * g + e], -e8) : v[8 * g + e] * enc;
             uint32_t packed;
             if constexpr (kSR) {
                 const u32x4 w = sr_words(seed, (uint64_t)row * cols + cb * B + 8 * g);
@@ -661,28 +662,26 @@ extern "C" nvfp4_status nvfp4_quantize_2d(const void* w, nvfp4_dtype dt, int64_t
         if (s) return s;
         src = out->amax;
     }
-    const uint32_t tiles = (uint32_t)((out->rows / 16) * (out->cols / 16));
     float* amax_t = out_t ? out_t->amax : nullptr;
     float* sdec_t = out_t ? out_t->s_dec : nullptr;
-    if (tiles == 0) {
+    if (out->rows == 0 || out->cols == 0) {
         hipLaunchKernelGGL(k_tensor_scalars, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
         if (out_t) hipLaunchKernelGGL(k_tensor_scalars, dim3(1), dim3(1), 0, st, src, amax_t, sdec_t);
         return launch_status();
     }
-    const FastDiv tpr = make_fastdiv((uint32_t)(out->cols / 16));
-    const int tiles_per_block = (kThreads / 64) * 4 * kQ2Groups;
-    const dim3 grid((tiles + tiles_per_block - 1) / tiles_per_block), block(kThreads);
+    const uint32_t rows = (uint32_t)out->rows, cols = (uint32_t)out->cols;
+    const uint32_t rpr = (cols + kQ2Region - 1) / kQ2Region;
+    const dim3 grid(rpr * ((rows + kQ2Region - 1) / kQ2Region)), block(kThreads);
     uint8_t* ct = out_t ? out_t->codes : nullptr;
     uint8_t* sct = out_t ? out_t->scales : nullptr;
-    const uint32_t rows = (uint32_t)out->rows, cols = (uint32_t)out->cols;
     if (dt == NVFP4_BF16)
         hipLaunchKernelGGL(k_quant2d<uint16_t>, grid, block, 0, st, static_cast<const uint16_t*>(w),
-                           ld, rows, cols, tiles, tpr, src, out->codes, out->scales, ct, sct,
-                           out->amax, out->s_dec, amax_t, sdec_t);
+                           ld, rows, cols, src, out->codes, out->scales, ct, sct, out->amax,
+                           out->s_dec, amax_t, sdec_t, rpr);
     else
         hipLaunchKernelGGL(k_quant2d<float>, grid, block, 0, st, static_cast<const float*>(w), ld,
-                           rows, cols, tiles, tpr, src, out->codes, out->scales, ct, sct,
-                           out->amax, out->s_dec, amax_t, sdec_t);
+                           rows, cols, src, out->codes, out->scales, ct, sct, out->amax,
+                           out->s_dec, amax_t, sdec_t, rpr);
     return launch_status();
 }
 
