@@ -102,6 +102,19 @@ NVFP4_API nvfp4_status nvfp4_amax(const void *x, nvfp4_dtype dt, int64_t rows, i
 NVFP4_API nvfp4_status nvfp4_hadamard_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
                                            uint64_t sign_seed, float *amax_out, void *stream);
 
+/* Accumulating forms of nvfp4_amax and nvfp4_hadamard_amax [P3 Come funziona NVFP4?: the
+ * per-tensor level of the scaling]: *amax_inout = max(*amax_inout, amax) with the same amax as
+ * above, and no zero-fill of *amax_inout first.  The caller initialises *amax_inout (0 gives the
+ * amax of x alone), which lets one amax cover several tensors or micro-batches and lets a caller
+ * clear many amax slots in one operation instead of one launch per slot.  *amax_inout must hold
+ * a non-negative, non-NaN float (it is raised by an unsigned atomic max on its bit pattern).  An
+ * empty x leaves it unchanged.  Same shape rules and errors as the non-accumulating calls. */
+NVFP4_API nvfp4_status nvfp4_amax_accumulate(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                             int64_t ld, float *amax_inout, void *stream);
+NVFP4_API nvfp4_status nvfp4_hadamard_amax_accumulate(const void *x, nvfp4_dtype dt, int64_t T, int64_t F,
+                                                      int64_t ld, uint64_t sign_seed, float *amax_inout,
+                                                      void *stream);
+
 /* 1D NVFP4 quantization of x [out->rows x out->cols] (row stride ld) into `out`
  * (layout NVFP4_BLK_1x16, cols % 16 == 0) [P1 Caracteristicas; P2 Describir].
  * amax_in: device pointer to the tensor amax to use, or NULL to compute it first (two passes).

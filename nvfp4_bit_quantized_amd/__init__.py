@@ -23,7 +23,8 @@ BLK_1x16, BLK_16x16, MX_1x32 = 0, 1, 2
 SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_quantize_1d",
            "nvfp4_quantize_2d", "nvfp4_hadamard_quantize", "nvfp4_dequantize", "nvfp4_gemm",
            "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual",
-           "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t")
+           "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t", "nvfp4_amax_accumulate",
+           "nvfp4_hadamard_amax_accumulate")
 
 
 class NvTensor(C.Structure):
@@ -49,6 +50,8 @@ def lib():
         L.nvfp4_status_string.argtypes = [i32]
         L.nvfp4_amax.argtypes = [P, i32, i64, i64, i64, P, P]
         L.nvfp4_hadamard_amax.argtypes = [P, i32, i64, i64, i64, u64, P, P]
+        L.nvfp4_amax_accumulate.argtypes = [P, i32, i64, i64, i64, P, P]
+        L.nvfp4_hadamard_amax_accumulate.argtypes = [P, i32, i64, i64, i64, u64, P, P]
         L.nvfp4_quantize_1d.argtypes = [P, i32, i64, P, i32, u64, T, P]
         L.nvfp4_quantize_2d.argtypes = [P, i32, i64, P, T, T, P]
         L.nvfp4_hadamard_quantize.argtypes = [P, i32, i64, u64, P, i32, u64, T, P]
@@ -152,6 +155,23 @@ def hadamard_amax(x: torch.Tensor, sign_seed: int, out: torch.Tensor | None = No
     _check("nvfp4_hadamard_amax", lib().nvfp4_hadamard_amax(_ptr(x), dt, x.shape[0], x.shape[1], ld,
                                                             sign_seed, _ptr(out), _stream(x.device)))
     return out
+
+
+def amax_accumulate(x: torch.Tensor, acc: torch.Tensor) -> torch.Tensor:
+    """acc (device fp32 [1], caller-initialised, >= 0) <- max(acc, max |x|); no zero-fill."""
+    x, dt, ld = _x(x)
+    _check("nvfp4_amax_accumulate", lib().nvfp4_amax_accumulate(_ptr(x), dt, x.shape[0], x.shape[1],
+                                                                ld, _ptr(acc), _stream(x.device)))
+    return acc
+
+
+def hadamard_amax_accumulate(x: torch.Tensor, sign_seed: int, acc: torch.Tensor) -> torch.Tensor:
+    """acc <- max(acc, amax of the random Hadamard transform of x); no zero-fill."""
+    x, dt, ld = _x(x)
+    _check("nvfp4_hadamard_amax_accumulate",
+           lib().nvfp4_hadamard_amax_accumulate(_ptr(x), dt, x.shape[0], x.shape[1], ld, sign_seed,
+                                                _ptr(acc), _stream(x.device)))
+    return acc
 
 
 def quantize_1d(x: torch.Tensor, rounding: int = RNE, seed: int = 0,

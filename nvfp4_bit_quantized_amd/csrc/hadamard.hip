@@ -70,7 +70,7 @@ __device__ __forceinline__ uint32_t rht_sign_mask(uint64_t sign_seed) {
 // The quantizer, whose codes keep the sign of zero, uses rht16 below.  The sign factors are the
 // same for every thread and kept as integer bit patterns so that they live in scalar registers.
 struct RhtPlan {
-    uint32_t s[32];     // +-1.0f bit patterns, stage by stage
+    uint32_t s[32];     // +-1.0f bit patterns, stage by stage (the amax uses the first 24)
 };
 
 __device__ __forceinline__ RhtPlan rht_plan(uint32_t sign_mask) {
@@ -91,11 +91,15 @@ __device__ __forceinline__ RhtPlan rht_plan(uint32_t sign_mask) {
     return p;
 }
 
-// In place: |v| <- |H16 D v| (signs and the 1/4 not applied).
-__device__ __forceinline__ void hd16_abs(float* v, const RhtPlan& p) {
+// max_i |(H16 D v)_i| (the 1/4 not applied), v overwritten.  The first three stages run the
+// butterfly network above.  In the last stage (pairs i, i + 8) the two results a + s b and
+// a - s b (s = +-1) have magnitudes |a| + |b| and ||a| - |b||; rounding is monotonic and
+// symmetric, so the larger rounded magnitude is fl(|a| + |b|) bit for bit, and the last stage
+// reduces to eight additions of magnitudes.
+__device__ __forceinline__ float hd16_absmax(float* v, const RhtPlan& p) {
     int k = 0;
 #pragma unroll
-    for (int hs = 1; hs < 16; hs <<= 1)
+    for (int hs = 1; hs < 8; hs <<= 1)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             if ((i & hs) == 0) {
@@ -105,6 +109,10 @@ __device__ __forceinline__ void hd16_abs(float* v, const RhtPlan& p) {
                 v[i + hs] = __builtin_fmaf(-sk, b, a);
                 ++k;
             }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[i]) + __builtin_fabsf(v[i + 8]));
+    return m;
 }
 
 // In place: v <- (1/4) H16 D v with D applied first and butterflies in the order h = 1, 2, 4, 8.
@@ -175,9 +183,7 @@ __device__ __forceinline__ void rht_amax_tile(const Tile16x8<T>& t16, const RhtP
 #pragma unroll
             for (int i = 0; i < 16; ++i) mp = fmaxf(mp, fabsf(v[i]));
         }
-        hd16_abs(v, plan);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        m = fmaxf(m, hd16_absmax(v, plan));
     }
 }
 
@@ -452,10 +458,11 @@ __global__ void k_fill2_rht(float* p, float* q) {
 
 // The amax of the transformed tensor into *dst and, if plain_dst is non-NULL, the amax of x
 // itself into *plain_dst, in one pass.
+// With `accumulate` false the destinations are zeroed first; otherwise the pass raises them.
 static nvfp4_status launch_rht_amax(const void* x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
                                     uint64_t sign_seed, float* dst, float* plain_dst,
-                                    hipStream_t st) {
-    hipLaunchKernelGGL(k_fill2_rht, dim3(1), dim3(1), 0, st, dst, plain_dst);
+                                    hipStream_t st, bool accumulate = false) {
+    if (!accumulate) hipLaunchKernelGGL(k_fill2_rht, dim3(1), dim3(1), 0, st, dst, plain_dst);
     if (T > 0 && F > 0) {
         const uint32_t tx = (uint32_t)((F + kAmaxFeat - 1) / kAmaxFeat);
         const uint32_t tiles = tx * (uint32_t)((T / 16 + kAmaxChunks - 1) / kAmaxChunks);
@@ -495,6 +502,16 @@ extern "C" nvfp4_status nvfp4_hadamard_amax(const void* x, nvfp4_dtype dt, int64
     s = check_amax_ptr(amax_out);
     if (s) return s;
     return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_out, nullptr, as_stream(stream));
+}
+
+extern "C" nvfp4_status nvfp4_hadamard_amax_accumulate(const void* x, nvfp4_dtype dt, int64_t T,
+                                                       int64_t F, int64_t ld, uint64_t sign_seed,
+                                                       float* amax_inout, void* stream) {
+    nvfp4_status s = check_rht_input(x, dt, T, F, ld);
+    if (s) return s;
+    s = check_amax_ptr(amax_inout);
+    if (s) return s;
+    return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_inout, nullptr, as_stream(stream), true);
 }
 
 extern "C" nvfp4_status nvfp4_dual_amax(const void* x, nvfp4_dtype dt, int64_t T, int64_t F,

@@ -536,9 +536,10 @@ static int stream_grid(uint32_t groups, int unroll = kUnroll) {
 }
 
 // Launch the amax pass for a dense [rows x cols] input into *dst (zeroed first).
+// The amax pass raises *dst to the tensor's amax; with `accumulate` false *dst is zeroed first.
 static nvfp4_status launch_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
-                                int64_t ld, float* dst, hipStream_t st) {
-    hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, dst, 0.0f);
+                                int64_t ld, float* dst, hipStream_t st, bool accumulate = false) {
+    if (!accumulate) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, dst, 0.0f);
     const int64_t g64 = rows * (cols / 8);
     if (g64 > 0) {
         const uint32_t groups = (uint32_t)g64;
@@ -575,15 +576,26 @@ extern "C" const char* nvfp4_status_string(nvfp4_status s) {
     return "unknown status";
 }
 
-extern "C" nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
-                                   int64_t ld, float* amax_out, void* stream) {
+static nvfp4_status amax_entry(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                               int64_t ld, float* amax_out, void* stream, bool accumulate) {
     nvfp4_status s = check_input(x, dt, rows, cols, ld);
     if (s) return s;
     if (!amax_out) return NVFP4_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(amax_out) & 3u) return NVFP4_ERR_ALIGN;
     if (cols % 8 != 0) return NVFP4_ERR_SHAPE;
     if (too_big(rows, cols)) return NVFP4_ERR_SHAPE;
-    return launch_amax(x, dt, rows, cols, ld, amax_out, as_stream(stream));
+    return launch_amax(x, dt, rows, cols, ld, amax_out, as_stream(stream), accumulate);
+}
+
+extern "C" nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                   int64_t ld, float* amax_out, void* stream) {
+    return amax_entry(x, dt, rows, cols, ld, amax_out, stream, false);
+}
+
+extern "C" nvfp4_status nvfp4_amax_accumulate(const void* x, nvfp4_dtype dt, int64_t rows,
+                                              int64_t cols, int64_t ld, float* amax_inout,
+                                              void* stream) {
+    return amax_entry(x, dt, rows, cols, ld, amax_inout, stream, true);
 }
 
 static nvfp4_status quantize_1d(const void* x, nvfp4_dtype dt, int64_t ld, const float* amax_in,
