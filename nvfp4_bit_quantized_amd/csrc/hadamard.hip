@@ -264,9 +264,13 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
                                                       const TensorScales& ts, uint64_t seed,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales) {
+    // Offsets of feature f0's output row; each further feature adds one row (64-bit additions
+    // instead of a 64-bit multiply per feature).
+    uint64_t idx = (uint64_t)rc.f0 * (uint64_t)Tn + (uint64_t)rc.c * 16;    // SR element index
+    uint8_t* cp = codes + rc.f0 * (Tn / 2) + rc.c * 8;
+    uint8_t* sp = scales + rc.f0 * (Tn / 16) + rc.c;
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-        const int64_t feat = rc.f0 + f;
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
@@ -282,7 +286,6 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
         for (int e = 0; e < 16; ++e) z[e] = v[e] * enc;
         uint32_t lo = 0, hi = 0;
         if constexpr (kSR) {
-            const uint64_t idx = (uint64_t)feat * (uint64_t)Tn + (uint64_t)rc.c * 16;
             const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
             const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
             lo = e2m1_sr_pack8(z, a);
@@ -291,10 +294,13 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
             lo = e2m1_rne_pack8(z);
             hi = e2m1_rne_pack8(z + 8);
         }
-        if (feat < F) {
-            *reinterpret_cast<uint2*>(codes + feat * (Tn / 2) + rc.c * 8) = make_uint2(lo, hi);
-            scales[feat * (Tn / 16) + rc.c] = (uint8_t)sb;
+        if (rc.f0 + f < F) {
+            *reinterpret_cast<uint2*>(cp) = make_uint2(lo, hi);
+            *sp = (uint8_t)sb;
         }
+        idx += (uint64_t)Tn;
+        cp += Tn / 2;
+        sp += Tn / 16;
     }
 }
 
@@ -309,6 +315,11 @@ __device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const R
                                                 uint8_t* __restrict__ codes,
                                                 uint8_t* __restrict__ scales) {
     const bool lead = (threadIdx.x & 1) == 0;
+    // Offsets of the chunk's first token row; each further row adds F elements.
+    const int64_t row0 = rc.c * 16;
+    uint64_t idx = (uint64_t)row0 * (uint64_t)F + (uint64_t)rc.f0;          // SR element index
+    uint8_t* cp = codes + row0 * (F / 2) + rc.f0 / 2;
+    uint8_t* sp = scales + row0 * (F / 16) + rc.f0 / 16;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         float y[8];
@@ -321,20 +332,22 @@ __device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const R
         uint32_t sb;
         float enc;
         block_scale(m, ts, sb, enc);
-        const int64_t row = rc.c * 16 + i;
         float z[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = y[e] * enc;
         uint32_t packed;
         if constexpr (kSR) {
-            const u32x4 w = sr_words(seed, (uint64_t)row * (uint64_t)F + (uint64_t)rc.f0);
+            const u32x4 w = sr_words(seed, idx);
             const uint32_t words[4] = {w.x, w.y, w.z, w.w};
             packed = e2m1_sr_pack8(z, words);
         } else {
             packed = e2m1_rne_pack8(z);
         }
-        *reinterpret_cast<uint32_t*>(codes + row * (F / 2) + rc.f0 / 2) = packed;
-        if (lead) scales[row * (F / 16) + rc.f0 / 16] = (uint8_t)sb;
+        *reinterpret_cast<uint32_t*>(cp) = packed;
+        if (lead) *sp = (uint8_t)sb;
+        idx += (uint64_t)F;
+        cp += F / 2;
+        sp += F / 16;
     }
 }
 
