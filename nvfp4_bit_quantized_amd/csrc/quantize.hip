@@ -18,6 +18,7 @@ namespace nvfp4 {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;     // groups per thread and trip in the amax / dequantize / MX kernels
 constexpr int kQUnroll = 2;    // blocks per thread in the NVFP4 1D quantizer (measured: 2 beats 1, 4, 8, 16)
+constexpr int kNoiseBlocks = 1024;   // grid cap of the quantizer with the noise sums
 
 // 8 input elements of one group as fp32.
 template <typename T> struct Group8;
@@ -125,21 +126,17 @@ __device__ __forceinline__ void e2m1_decode8(uint32_t w, float* v) {
 // values times s_enc = 2688 / amax (at most 5376 in magnitude, so no fp32 overflow or early
 // underflow), each 16-element block is summed in fp32, blocks are accumulated in fp64, and each
 // workgroup adds its two totals, divided by s_enc^2, atomically.
+// The work of one k_quant1d thread on kQUnroll blocks starting at block `base` (spaced a
+// workgroup apart): all loads first, then per block the scale, the codes and, with kNoise, the
+// block's contributions to the two noise sums.
 template <typename T, bool kSR, bool kNoise>
-__global__ void __launch_bounds__(kThreads)
-k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uint32_t cols,
-          const float* __restrict__ amax_src, uint64_t seed, uint2* __restrict__ codes,
-          uint8_t* __restrict__ scales, float* amax_out, float* sdec_out, double* sums) {
-    const float A = *amax_src;
-    const TensorScales ts = tensor_scales(A);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *amax_out = A;
-        *sdec_out = ts.s_dec;
-    }
-    const uint32_t base = blockIdx.x * kThreads * kQUnroll + threadIdx.x;
+__device__ __forceinline__ void quant1d_blocks(const T* __restrict__ x, int64_t ld, uint32_t blocks,
+                                               FastDiv bpr, uint32_t cols, const TensorScales& ts,
+                                               uint64_t seed, uint2* __restrict__ codes,
+                                               uint8_t* __restrict__ scales, uint32_t base,
+                                               double& g2, double& e2) {
     float y[kQUnroll][16];
     uint32_t row[kQUnroll], cb[kQUnroll];
-    double g2 = 0.0, e2 = 0.0;
 #pragma unroll
     for (int u = 0; u < kQUnroll; ++u) {
         uint32_t b = base + u * kThreads;
@@ -193,6 +190,32 @@ k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uin
                 e2 += (double)be;
             }
         }
+    }
+}
+
+template <typename T, bool kSR, bool kNoise>
+__global__ void __launch_bounds__(kThreads)
+k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uint32_t cols,
+          const float* __restrict__ amax_src, uint64_t seed, uint2* __restrict__ codes,
+          uint8_t* __restrict__ scales, float* amax_out, float* sdec_out, double* sums) {
+    const float A = *amax_src;
+    const TensorScales ts = tensor_scales(A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *amax_out = A;
+        *sdec_out = ts.s_dec;
+    }
+    // With kNoise the grid is capped and each workgroup strides over the blocks, so that few
+    // workgroups publish sums (same-address fp64 atomics serialize); otherwise the grid covers
+    // every block once.
+    double g2 = 0.0, e2 = 0.0;
+    if constexpr (kNoise) {
+        for (uint32_t wbase = blockIdx.x * kThreads * kQUnroll; wbase < blocks;
+             wbase += gridDim.x * kThreads * kQUnroll)
+            quant1d_blocks<T, kSR, kNoise>(x, ld, blocks, bpr, cols, ts, seed, codes, scales,
+                                           wbase + threadIdx.x, g2, e2);
+    } else {
+        quant1d_blocks<T, kSR, kNoise>(x, ld, blocks, bpr, cols, ts, seed, codes, scales,
+                                       blockIdx.x * kThreads * kQUnroll + threadIdx.x, g2, e2);
     }
     if constexpr (kNoise) {
 #pragma unroll
@@ -535,8 +558,7 @@ static int stream_grid(uint32_t groups, int unroll = kUnroll) {
     return (int)(n < 1 ? 1 : n);
 }
 
-// Launch the amax pass for a dense [rows x cols] input into *dst (zeroed first).
-// The amax pass raises *dst to the tensor's amax; with `accumulate` false *dst is zeroed first.
+// Launch the amax pass for a dense [rows x cols] input: it raises *dst to the tensor's amax; with `accumulate` false *dst is zeroed first.
 static nvfp4_status launch_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
                                 int64_t ld, float* dst, hipStream_t st, bool accumulate = false) {
     if (!accumulate) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, dst, 0.0f);
@@ -620,7 +642,8 @@ static nvfp4_status quantize_1d(const void* x, nvfp4_dtype dt, int64_t ld, const
         return launch_status();
     }
     const FastDiv bpr = make_fastdiv((uint32_t)(out->cols / 16));
-    const dim3 grid(stream_grid(blocks, kQUnroll)), block(kThreads);
+    const int full = stream_grid(blocks, kQUnroll);
+    const dim3 grid(sums && full > kNoiseBlocks ? kNoiseBlocks : full), block(kThreads);
     uint2* codes = reinterpret_cast<uint2*>(out->codes);
     const uint32_t cols = (uint32_t)out->cols;
 #define NVFP4_Q1(T, SRV, NZ)                                                                     \

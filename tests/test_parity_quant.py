@@ -84,7 +84,11 @@ def test_quantize_1d_sr_deterministic_and_seeded(nv):
 
 @pytest.mark.parametrize("name,make", [("w_ragged", lambda: W.weight((48, 80), 21)),
                                        ("w_fp32", lambda: W.small_fp32((64, 32), 22)),
-                                       ("w_rect", lambda: W.weight((160, 96), 23))])
+                                       ("w_rect", lambda: W.weight((160, 96), 23)),
+                                       # several 128x128 workgroup regions in both dimensions,
+                                       # with 16-wide tails
+                                       ("w_regions", lambda: W.weight((272, 400), 24)),
+                                       ("w_regions_fp32", lambda: W.small_fp32((400, 272), 25))])
 def test_quantize_2d_small(nv, orc, name, make):
     w = make()
     g, gt = nv.quantize_2d(w.to(DEV), transposed=True)
@@ -93,6 +97,17 @@ def test_quantize_2d_small(nv, orc, name, make):
     np.testing.assert_array_equal(_host(gt.codes), o["codes_t"])
     np.testing.assert_array_equal(_host(gt.scales), o["scales_t"])
     assert gt.s_dec.item() == o["s_dec"]
+
+
+def test_quantize_2d_strided(nv, orc):
+    """A weight that is a column slice of a wider matrix (row stride > cols)."""
+    big = W.weight((144, 320), 26)
+    w = big[:, 48:48 + 256]
+    g, gt = nv.quantize_2d(big.to(DEV)[:, 48:48 + 256], transposed=True)
+    o = orc.quantize_2d(W.bits(w.contiguous()))
+    _same_q(g, o, "strided")
+    np.testing.assert_array_equal(_host(gt.codes), o["codes_t"])
+    np.testing.assert_array_equal(_host(gt.scales), o["scales_t"])
 
 
 @pytest.mark.parametrize("rounding", [0, 1])
