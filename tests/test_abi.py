@@ -93,6 +93,19 @@ def test_quantize_2d_and_hadamard_validation(L):
     assert L.nvfp4_amax(FAKE, nv.BF16, 4, 16, 16, FAKE + 1, None) == nv.ERR_ALIGN
 
 
+def test_amax_accumulate_validation(L):
+    """The accumulating amax calls validate like the plain ones (nothing is enqueued)."""
+    assert L.nvfp4_amax_accumulate(None, nv.BF16, 4, 16, 16, FAKE, None) == nv.ERR_NULL
+    assert L.nvfp4_amax_accumulate(FAKE, nv.BF16, 4, 16, 16, None, None) == nv.ERR_NULL
+    assert L.nvfp4_amax_accumulate(FAKE, nv.BF16, 4, 16, 16, FAKE + 1, None) == nv.ERR_ALIGN
+    assert L.nvfp4_amax_accumulate(FAKE, nv.BF16, 4, 12, 16, FAKE, None) == nv.ERR_SHAPE
+    assert L.nvfp4_amax_accumulate(FAKE, 7, 4, 16, 16, FAKE, None) == nv.ERR_DTYPE
+    assert L.nvfp4_hadamard_amax_accumulate(FAKE, nv.BF16, 40, 16, 16, 1, FAKE, None) == nv.ERR_SHAPE
+    assert L.nvfp4_hadamard_amax_accumulate(FAKE, nv.BF16, 32, 12, 16, 1, FAKE, None) == nv.ERR_SHAPE
+    assert L.nvfp4_hadamard_amax_accumulate(FAKE, nv.BF16, 32, 16, 16, 1, None, None) == nv.ERR_NULL
+    assert L.nvfp4_hadamard_amax_accumulate(FAKE, nv.BF16, 32, 16, 16, 1, FAKE + 2, None) == nv.ERR_ALIGN
+
+
 def test_gemm_validation(L):
     a, b = _q(64, 64), _q(32, 48)
     assert L.nvfp4_gemm(C.byref(a), C.byref(b), FAKE, nv.F32, 32, None) == nv.ERR_SHAPE
