@@ -558,7 +558,8 @@ static int stream_grid(uint32_t groups, int unroll = kUnroll) {
     return (int)(n < 1 ? 1 : n);
 }
 
-// Launch the amax pass for a dense [rows x cols] input: it raises *dst to the tensor's amax; with `accumulate` false *dst is zeroed first.
+// Launch the amax pass for a dense [rows x cols] input: it raises *dst to the tensor's amax;
+// with `accumulate` false *dst is zeroed first.
 static nvfp4_status launch_amax(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
                                 int64_t ld, float* dst, hipStream_t st, bool accumulate = false) {
     if (!accumulate) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, dst, 0.0f);
