@@ -359,12 +359,6 @@ k_quant2d(const T* __restrict__ w, int64_t ld, uint32_t rows, uint32_t cols,
 }
 
 // ---- dequantization -------------------------------------------------------------------------
-__device__ __forceinline__ float e2m1_decode(uint32_t c) {
-    uint32_t m = c & 7u;
-    float mag = m < 2 ? 0.5f * (float)m : __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
-    return (c & 8u) ? -mag : mag;
-}
-
 template <bool kBF16Out>
 __global__ void __launch_bounds__(kThreads)
 k_dequant(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales, int layout,
@@ -372,34 +366,45 @@ k_dequant(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales
           void* __restrict__ out, int64_t ld) {
     const float sdec = layout == MXFP4_BLK_1x32 ? 1.0f : *sdec_src;
     const uint32_t base = blockIdx.x * kThreads * kUnroll + threadIdx.x;
+    // All loads first (groups past the end load the last group and store nothing).
+    uint32_t c[kUnroll], sb[kUnroll], row[kUnroll], cg[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t g = base + u * kThreads;
-        if (g >= groups) break;
-        const uint32_t row = fastdiv(g, gpr), cg = g - row * gpr.d;
-        const uint32_t c = codes[g];
+        uint32_t g = base + u * kThreads;
+        g = g < groups ? g : groups - 1;
+        row[u] = fastdiv(g, gpr);
+        cg[u] = g - row[u] * gpr.d;
+        c[u] = codes[g];
+        const int64_t si = layout == MXFP4_BLK_1x32 ? (int64_t)row[u] * (cols / 32) + cg[u] / 4
+                         : layout == NVFP4_BLK_16x16 ? (int64_t)(row[u] / 16) * (cols / 16) + cg[u] / 2
+                                                     : (int64_t)row[u] * (cols / 16) + cg[u] / 2;
+        sb[u] = scales[si];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
         float v[8];
+        e2m1_decode8(c[u], v);                       // exact E2M1 values
         if (layout == MXFP4_BLK_1x32) {
-            const int e = (int)scales[(int64_t)row * (cols / 32) + cg / 4] - 127;
+            const int e = (int)sb[u] - 127;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = __builtin_amdgcn_ldexpf(e2m1_decode(c >> (4 * i)), e);
+            for (int i = 0; i < 8; ++i) v[i] = __builtin_amdgcn_ldexpf(v[i], e);
         } else {
-            const uint32_t sb = layout == NVFP4_BLK_16x16
-                                    ? scales[(int64_t)(row / 16) * (cols / 16) + cg / 2]
-                                    : scales[(int64_t)row * (cols / 16) + cg / 2];
-            const float s = e4m3_decode(sb);
+            const float s = e4m3_decode(sb[u]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (e2m1_decode(c >> (4 * i)) * s) * sdec;
+            for (int i = 0; i < 8; ++i) v[i] = (v[i] * s) * sdec;
         }
+        if (base + u * kThreads >= groups) continue;
         if constexpr (kBF16Out) {
             uint4 o;
             o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
             o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
             o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
             o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)row * ld + cg * 8) = o;
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)row[u] * ld +
+                                      cg[u] * 8) = o;
         } else {
-            float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)row * ld + cg * 8);
+            float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) +
+                                                  (int64_t)row[u] * ld + cg[u] * 8);
             o[0] = make_float4(v[0], v[1], v[2], v[3]);
             o[1] = make_float4(v[4], v[5], v[6], v[7]);
         }
