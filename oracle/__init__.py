@@ -77,6 +77,8 @@ def lib():
         L.or_rht16.argtypes = [P, P]
         L.or_hadamard_amax.restype = i32
         L.or_hadamard_amax.argtypes = [P, i32, i64, i64, i64, u64, P]
+        L.or_hadamard_transform.restype = i32
+        L.or_hadamard_transform.argtypes = [P, i32, i64, i64, i64, u64, P]
         L.or_hadamard_quantize.restype = i32
         L.or_hadamard_quantize.argtypes = [P, i32, i64, i64, i64, u64, P, i32, u64, P, P, P, P]
         L.or_dequantize.restype = i32
@@ -257,6 +259,17 @@ def hadamard_amax(x: np.ndarray, sign_seed: int) -> float:
     out = np.zeros(1, dtype=np.float32)
     _check(lib().or_hadamard_amax(_ptr(x), dt, T, F, F, int(sign_seed), _ptr(out)), "hadamard_amax")
     return float(out[0])
+
+
+def hadamard_transform(x: np.ndarray, sign_seed: int) -> np.ndarray:
+    """x [T x F] -> the transformed, transposed tensor y [F x T] float32 that
+    ``hadamard_quantize`` encodes: y[f, 16c:16c+16] = rht16(x[16c:16c+16, f])."""
+    x, dt = _input(x)
+    T, F = x.shape
+    y = np.zeros((F, T), dtype=np.float32)
+    _check(lib().or_hadamard_transform(_ptr(x), dt, T, F, F, int(sign_seed), _ptr(y)),
+           "hadamard_transform")
+    return y
 
 
 def hadamard_quantize(x: np.ndarray, sign_seed: int, rounding: int = RNE, seed: int = 0,

@@ -451,6 +451,28 @@ int or_hadamard_amax(const void *x, int dtype, int64_t T, int64_t F, int64_t ld,
     return OR_OK;
 }
 
+/* The transformed tensor itself, transposed: y [F x T] fp32 with y[f][16c .. 16c + 15] =
+ * (1/4) H16 D x[16c .. 16c + 15][f] (or_rht16).  This is the tensor the Hadamard quantizer
+ * encodes; the quantization-noise diagnostic of that quantizer compares against it. */
+int or_hadamard_transform(const void *x, int dtype, int64_t T, int64_t F, int64_t ld,
+                          uint64_t sign_seed, float *y_out)
+{
+    if (T % 16 != 0 || T < 0 || F < 0 || ld < F) return OR_ERR_SHAPE;
+    int d[16];
+    or_rht_signs(sign_seed, d);
+    for (int64_t f = 0; f < F; ++f)
+        for (int64_t c = 0; c < T / 16; ++c) {
+            float y[16];
+            for (int i = 0; i < 16; ++i) {
+                y[i] = load_elem(x, dtype, (c * 16 + i) * ld + f);
+                if (!isfinite(y[i])) return OR_ERR_NONFINITE;
+            }
+            or_rht16(y, d);
+            for (int i = 0; i < 16; ++i) y_out[f * T + c * 16 + i] = y[i];
+        }
+    return OR_OK;
+}
+
 /* Hadamard + transpose + 1D quantize of one wgrad operand x [T tokens x F features] (row
  * stride ld).  Output is feature-major so that the reduction dimension (tokens) is contiguous:
  * codes [F x T/2], scales [F x T/16]; element (f, t) has SR index f * T + t. */

@@ -70,3 +70,24 @@ def test_hadamard_quantize_is_transform_then_transposed_1d(orc, rounding):
     np.testing.assert_array_equal(q["codes"], ref["codes"])
     np.testing.assert_array_equal(q["scales"], ref["scales"])
     assert q["s_dec"] == ref["s_dec"]
+
+
+def test_hadamard_transform_is_rht16_per_chunk_and_feeds_the_quantizer(orc):
+    """The transposed transform equals rht16 applied to every 16-token chunk of every feature,
+    its largest magnitude is the Hadamard amax, and its 1D quantization is the Hadamard
+    quantizer's output."""
+    x = W.grad((64, 24), 77)
+    xb = W.bits(x)
+    sign_seed = 0x51E4
+    y = orc.hadamard_transform(xb, sign_seed)
+    d = orc.rht_signs(sign_seed)
+    xv = orc.values(xb).astype(np.float32)
+    assert y.shape == (24, 64)
+    for f in range(24):
+        for c in range(4):
+            np.testing.assert_array_equal(y[f, 16 * c:16 * c + 16], orc.rht16(xv[16 * c:16 * c + 16, f], d))
+    assert float(np.abs(y).max()) == orc.hadamard_amax(xb, sign_seed)
+    q = orc.hadamard_quantize(xb, sign_seed, rounding=1, seed=9)
+    ref = orc.quantize_1d(y, rounding=1, seed=9)
+    np.testing.assert_array_equal(q["codes"], ref["codes"])
+    np.testing.assert_array_equal(q["scales"], ref["scales"])
