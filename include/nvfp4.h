@@ -158,6 +158,20 @@ NVFP4_API nvfp4_status nvfp4_hadamard_quantize(const void *x, nvfp4_dtype dt, in
                                                const float *amax_in, nvfp4_round rnd, uint64_t seed,
                                                const nvfp4_tensor *out, void *stream);
 
+/* nvfp4_hadamard_quantize plus, in the same pass, the quantization-noise diagnostic of
+ * [P2 Describir: quantized training loses efficiency once the gradient norm falls below about
+ * sqrt(3) times the quantization noise] for the tensor this call encodes, the transformed
+ * y = (1/4) H16 D x: sums[0] = sum of y^2 and sums[1] = sum of (Q(y) - y)^2, Q(y) the dequantized
+ * value (as nvfp4_dequantize computes it in fp32).  Since (1/4) H16 D is orthogonal, sum y^2
+ * equals sum x^2 up to rounding.  sums: device, two doubles, 8-byte aligned, overwritten.
+ * Accumulated as in nvfp4_quantize_1d_noise (fp32 per 16-element block on values times s_enc,
+ * fp64 across blocks, device atomics: the last bits vary from run to run); codes and scales are
+ * exactly those of nvfp4_hadamard_quantize. */
+NVFP4_API nvfp4_status nvfp4_hadamard_quantize_noise(const void *x, nvfp4_dtype dt, int64_t ld,
+                                                     uint64_t sign_seed, const float *amax_in,
+                                                     nvfp4_round rnd, uint64_t seed,
+                                                     const nvfp4_tensor *out, double *sums, void *stream);
+
 /* amax of x [T x F] and of its random Hadamard transform (as in nvfp4_hadamard_quantize) in one
  * read of x: *amax_out = max |x|, *amax_t_out = max |(1/4) H16 D x|.  T % 16 == 0, F % 8 == 0;
  * the two outputs must be distinct (else NVFP4_ERR_SHAPE). */

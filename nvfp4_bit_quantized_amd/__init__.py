@@ -24,7 +24,7 @@ SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_qu
            "nvfp4_quantize_2d", "nvfp4_hadamard_quantize", "nvfp4_dequantize", "nvfp4_gemm",
            "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual",
            "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t", "nvfp4_amax_accumulate",
-           "nvfp4_hadamard_amax_accumulate")
+           "nvfp4_hadamard_amax_accumulate", "nvfp4_hadamard_quantize_noise")
 
 
 class NvTensor(C.Structure):
@@ -55,6 +55,7 @@ def lib():
         L.nvfp4_quantize_1d.argtypes = [P, i32, i64, P, i32, u64, T, P]
         L.nvfp4_quantize_2d.argtypes = [P, i32, i64, P, T, T, P]
         L.nvfp4_hadamard_quantize.argtypes = [P, i32, i64, u64, P, i32, u64, T, P]
+        L.nvfp4_hadamard_quantize_noise.argtypes = [P, i32, i64, u64, P, i32, u64, T, P, P]
         L.nvfp4_dequantize.argtypes = [T, P, i32, i64, P]
         L.nvfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.mxfp4_quantize_1d.argtypes = [P, i32, i64, i32, u64, T, P]
@@ -252,6 +253,22 @@ def hadamard_quantize(x: torch.Tensor, sign_seed: int, rounding: int = RNE, seed
            lib().nvfp4_hadamard_quantize(_ptr(x), dt, ld, sign_seed, _ptr(amax_in), rounding, seed,
                                          C.byref(d), _stream(x.device)))
     return q
+
+
+def hadamard_quantize_noise(x: torch.Tensor, sign_seed: int, rounding: int = SR, seed: int = 0,
+                            amax_in: torch.Tensor | None = None, out: QTensor | None = None,
+                            sums: torch.Tensor | None = None):
+    """hadamard_quantize plus the noise diagnostic of the transformed tensor y it encodes:
+    (QTensor [F x T], sums) with sums a device float64 [2] = (sum y^2, sum (Q(y) - y)^2)."""
+    x, dt, ld = _x(x)
+    T, F = x.shape
+    q = QTensor.empty(F, T, BLK_1x16, x.device) if out is None else out
+    sums = torch.empty(2, dtype=torch.float64, device=x.device) if sums is None else sums
+    d = q.desc()
+    _check("nvfp4_hadamard_quantize_noise",
+           lib().nvfp4_hadamard_quantize_noise(_ptr(x), dt, ld, sign_seed, _ptr(amax_in), rounding,
+                                               seed, C.byref(d), _ptr(sums), _stream(x.device)))
+    return q, sums
 
 
 def dual_amax(x: torch.Tensor, sign_seed: int, out: torch.Tensor | None = None,

@@ -18,6 +18,7 @@
 
 #include "device_codecs.hpp"
 #include "host_util.hpp"
+#include "noise.hpp"
 
 namespace nvfp4 {
 
@@ -145,13 +146,17 @@ struct RhtCoords {
     bool valid;
 };
 
-__device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
+__device__ __forceinline__ RhtCoords rht_coords_at(int64_t T, int64_t F, uint32_t bx, uint32_t by) {
     RhtCoords rc;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    rc.f0 = (int64_t)blockIdx.x * kFeatPerBlock + (lane & 7) * 8;
-    rc.c = (int64_t)blockIdx.y * kChunksPerBlock + wave * 8 + (lane >> 3);
+    rc.f0 = (int64_t)bx * kFeatPerBlock + (lane & 7) * 8;
+    rc.c = (int64_t)by * kChunksPerBlock + wave * 8 + (lane >> 3);
     rc.valid = rc.f0 < F && rc.c * 16 < T;
     return rc;
+}
+
+__device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
+    return rht_coords_at(T, F, blockIdx.x, blockIdx.y);
 }
 
 // Persistent over (64-feature x 512-token) tiles, at most kRhtAmaxBlocks workgroups, each
@@ -258,12 +263,13 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
 
 // The transposed copy of one thread's tile: for each of its 8 features, the 16 tokens of its
 // chunk through (1/4) H16 D, one NVFP4 block of row `feature` of the [F x T] output.
-template <typename T, bool kSR>
+template <typename T, bool kSR, bool kNoise>
 __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, const RhtCoords& rc,
                                                       int64_t Tn, int64_t F, uint32_t mask,
                                                       const TensorScales& ts, uint64_t seed,
                                                       uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales) {
+                                                      uint8_t* __restrict__ scales, double& g2,
+                                                      double& e2) {
     // Offsets of feature f0's output row; each further feature adds one row (64-bit additions
     // instead of a 64-bit multiply per feature).
     uint64_t idx = (uint64_t)rc.f0 * (uint64_t)Tn + (uint64_t)rc.c * 16;    // SR element index
@@ -297,6 +303,7 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
         if (rc.f0 + f < F) {
             *reinterpret_cast<uint2*>(cp) = make_uint2(lo, hi);
             *sp = (uint8_t)sb;
+            if constexpr (kNoise) block_noise(v, lo, hi, sb, ts, g2, e2);
         }
         idx += (uint64_t)Tn;
         cp += Tn / 2;
@@ -351,23 +358,42 @@ __device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const R
     }
 }
 
-template <typename T, bool kSR>
+template <typename T, bool kSR, bool kNoise>
 __global__ void __launch_bounds__(kRhtThreads)
 k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
             const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
-            uint8_t* __restrict__ scales, float* amax_out, float* sdec_out) {
+            uint8_t* __restrict__ scales, float* amax_out, float* sdec_out, double* sums,
+            uint32_t chunk_blocks) {
     const float A = *amax_src;
     const TensorScales ts = tensor_scales(A);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
         *amax_out = A;
         *sdec_out = ts.s_dec;
     }
-    const RhtCoords rc = rht_coords(Tn, F);
-    if (!rc.valid) return;
     const uint32_t mask = rht_sign_mask(sign_seed);
-    Tile16x8<T> tile;
-    tile.load(x + rc.c * 16 * ld + rc.f0, ld);
-    quant_tile_transposed<T, kSR>(tile, rc, Tn, F, mask, ts, seed, codes, scales);
+    double g2 = 0.0, e2 = 0.0;
+    if constexpr (kNoise) {
+        // The grid is capped in y and each workgroup strides over the chunk blocks of its
+        // feature block, so that few workgroups publish noise sums (same-address fp64 atomics
+        // serialize).  Every thread reaches the workgroup reduction.
+        for (uint32_t by = blockIdx.y; by < chunk_blocks; by += gridDim.y) {
+            const RhtCoords rc = rht_coords_at(Tn, F, blockIdx.x, by);
+            if (rc.valid) {
+                Tile16x8<T> tile;
+                tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+                quant_tile_transposed<T, kSR, true>(tile, rc, Tn, F, mask, ts, seed, codes, scales,
+                                                    g2, e2);
+            }
+        }
+        publish_noise<kRhtThreads>(g2, e2, ts, sums);
+    } else {
+        const RhtCoords rc = rht_coords(Tn, F);
+        if (!rc.valid) return;
+        Tile16x8<T> tile;
+        tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+        quant_tile_transposed<T, kSR, false>(tile, rc, Tn, F, mask, ts, seed, codes, scales, g2,
+                                             e2);
+    }
 }
 
 // Fused dual-orientation quantizer: one read of x gives the row-wise copy [T x F] (as the 1D
@@ -395,7 +421,9 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
     Tile16x8<T> tile;
     tile.load(x + rc.c * 16 * ld + rc.f0, ld);
     quant_tile_rows<T, kSR>(tile, rc, F, ts, seed, codes, scales);
-    quant_tile_transposed<T, kSR>(tile, rc, Tn, F, mask, tst, seed_t, codes_t, scales_t);
+    double g2 = 0.0, e2 = 0.0;             // unused: the dual quantizer has no noise sums
+    quant_tile_transposed<T, kSR, false>(tile, rc, Tn, F, mask, tst, seed_t, codes_t, scales_t, g2,
+                                         e2);
 }
 
 // MXFP4 quantization of x^T [P3 NVFP4 in pratica: MXFP4, 32-element blocks with power-of-two
@@ -462,6 +490,11 @@ static nvfp4_status check_rht_input(const void* x, nvfp4_dtype dt, int64_t T, in
     const int64_t amax_tiles = ((F + kAmaxFeat - 1) / kAmaxFeat) * ((T / 16 + kAmaxChunks - 1) / kAmaxChunks);
     if (F >= (1ll << 31) || gy > 65535 || amax_tiles >= (1ll << 31)) return NVFP4_ERR_SHAPE;
     return NVFP4_OK;
+}
+
+__global__ void k_fill2_f64(double* p) {
+    p[0] = 0.0;
+    p[1] = 0.0;
 }
 
 __global__ void k_fill2_rht(float* p, float* q) {
@@ -537,38 +570,68 @@ extern "C" nvfp4_status nvfp4_dual_amax(const void* x, nvfp4_dtype dt, int64_t T
     return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_t_out, amax_out, as_stream(stream));
 }
 
-extern "C" nvfp4_status nvfp4_hadamard_quantize(const void* x, nvfp4_dtype dt, int64_t ld,
-                                                uint64_t sign_seed, const float* amax_in,
-                                                nvfp4_round rnd, uint64_t seed,
-                                                const nvfp4_tensor* out, void* stream) {
+constexpr uint32_t kNoiseWorkgroups = 1024;   // target grid size of the quantizer with noise sums
+
+static nvfp4_status hadamard_quantize(const void* x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
+                                      const float* amax_in, nvfp4_round rnd, uint64_t seed,
+                                      const nvfp4_tensor* out, double* sums, hipStream_t st) {
     nvfp4_status s = check_q(out, NVFP4_BLK_1x16, true);
     if (s) return s;
     const int64_t F = out->rows, T = out->cols;
     s = check_rht_input(x, dt, T, F, ld);
     if (s) return s;
     if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
-    hipStream_t st = as_stream(stream);
     const float* src = amax_in;
     if (!src) {
         s = launch_rht_amax(x, dt, T, F, ld, sign_seed, out->amax, nullptr, st);
         if (s) return s;
         src = out->amax;
     }
+    if (sums) hipLaunchKernelGGL(k_fill2_f64, dim3(1), dim3(1), 0, st, sums);
     if (T == 0 || F == 0) {
         hipLaunchKernelGGL(k_scalars_rht, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
         return launch_status();
     }
-    const dim3 grid = rht_grid(T, F), block(kRhtThreads);
-#define NVFP4_RQ(TT, SRV)                                                                         \
-    hipLaunchKernelGGL((k_rht_quant<TT, SRV>), grid, block, 0, st, static_cast<const TT*>(x), T, F, \
-                       ld, sign_seed, src, seed, out->codes, out->scales, out->amax, out->s_dec)
-    if (dt == NVFP4_BF16) {
-        if (rnd == NVFP4_SR) NVFP4_RQ(uint16_t, true); else NVFP4_RQ(uint16_t, false);
-    } else {
-        if (rnd == NVFP4_SR) NVFP4_RQ(float, true); else NVFP4_RQ(float, false);
+    dim3 grid = rht_grid(T, F);
+    const uint32_t chunk_blocks = grid.y;
+    if (sums) {
+        const uint32_t cap = (kNoiseWorkgroups + grid.x - 1) / grid.x;
+        grid.y = chunk_blocks < cap ? chunk_blocks : cap;
     }
+    const dim3 block(kRhtThreads);
+#define NVFP4_RQ(TT, SRV, NZ)                                                                      \
+    hipLaunchKernelGGL((k_rht_quant<TT, SRV, NZ>), grid, block, 0, st, static_cast<const TT*>(x), T, \
+                       F, ld, sign_seed, src, seed, out->codes, out->scales, out->amax, out->s_dec, \
+                       sums, chunk_blocks)
+#define NVFP4_RQR(TT, NZ)                                                                          \
+    if (rnd == NVFP4_SR) NVFP4_RQ(TT, true, NZ); else NVFP4_RQ(TT, false, NZ)
+    if (dt == NVFP4_BF16) {
+        if (sums) NVFP4_RQR(uint16_t, true); else NVFP4_RQR(uint16_t, false);
+    } else {
+        if (sums) NVFP4_RQR(float, true); else NVFP4_RQR(float, false);
+    }
+#undef NVFP4_RQR
 #undef NVFP4_RQ
     return launch_status();
+}
+
+extern "C" nvfp4_status nvfp4_hadamard_quantize(const void* x, nvfp4_dtype dt, int64_t ld,
+                                                uint64_t sign_seed, const float* amax_in,
+                                                nvfp4_round rnd, uint64_t seed,
+                                                const nvfp4_tensor* out, void* stream) {
+    return hadamard_quantize(x, dt, ld, sign_seed, amax_in, rnd, seed, out, nullptr,
+                             as_stream(stream));
+}
+
+extern "C" nvfp4_status nvfp4_hadamard_quantize_noise(const void* x, nvfp4_dtype dt, int64_t ld,
+                                                      uint64_t sign_seed, const float* amax_in,
+                                                      nvfp4_round rnd, uint64_t seed,
+                                                      const nvfp4_tensor* out, double* sums,
+                                                      void* stream) {
+    if (!sums) return NVFP4_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(sums) & 7u) return NVFP4_ERR_ALIGN;
+    return hadamard_quantize(x, dt, ld, sign_seed, amax_in, rnd, seed, out, sums,
+                             as_stream(stream));
 }
 
 extern "C" nvfp4_status nvfp4_quantize_dual(const void* x, nvfp4_dtype dt, int64_t ld,

@@ -12,6 +12,7 @@
 
 #include "device_codecs.hpp"
 #include "host_util.hpp"
+#include "noise.hpp"
 
 namespace nvfp4 {
 
@@ -103,17 +104,6 @@ static int amax_grid(uint32_t groups) {
     return (int)(need < 1 ? 1 : (need < kAmaxBlocks ? need : kAmaxBlocks));
 }
 
-// Values of eight packed E2M1 codes (element 2j in the low nibble of byte j); with a unit scale
-// v_cvt_scalef32_pk_f32_fp4 returns the exact E2M1 values.
-__device__ __forceinline__ void e2m1_decode8(uint32_t w, float* v) {
-    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
-    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
-}
-
 // ---- 1D quantization [P1 Caracteristicas; P2 Describir] ---------------------------------------
 // One lane owns one whole 16-element block: two 16-byte loads (bf16), one 8-byte code store and
 // one scale byte.  Each thread handles kQUnroll blocks spaced a workgroup apart, all loads first.
@@ -125,7 +115,8 @@ __device__ __forceinline__ void e2m1_decode8(uint32_t w, float* v) {
 // Q(x) = fl(fl(v * scale) * s_dec) is the dequantized value.  The squares are taken of the
 // values times s_enc = 2688 / amax (at most 5376 in magnitude, so no fp32 overflow or early
 // underflow), each 16-element block is summed in fp32, blocks are accumulated in fp64, and each
-// workgroup adds its two totals, divided by s_enc^2, atomically.
+// workgroup adds its two totals, divided by s_enc^2, atomically (noise.hpp).
+
 // The work of one k_quant1d thread on kQUnroll blocks starting at block `base` (spaced a
 // workgroup apart): all loads first, then per block the scale, the codes and, with kNoise, the
 // block's contributions to the two noise sums.
@@ -173,22 +164,7 @@ __device__ __forceinline__ void quant1d_blocks(const T* __restrict__ x, int64_t 
         if (b < blocks) {
             codes[b] = make_uint2(lo, hi);       // blocks are dense in the code array
             scales[b] = (uint8_t)sb;
-            if constexpr (kNoise) {
-                const float sc = e4m3_decode(sb);
-                float v[16];
-                e2m1_decode8(lo, v);
-                e2m1_decode8(hi, v + 8);
-                float bg = 0.0f, be = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float d = (v[e] * sc) * ts.s_dec - y[u][e];
-                    const float ys = y[u][e] * ts.s_enc, ds = d * ts.s_enc;   // |.| <= 5376
-                    bg += ys * ys;
-                    be += ds * ds;
-                }
-                g2 += (double)bg;
-                e2 += (double)be;
-            }
+            if constexpr (kNoise) block_noise(y[u], lo, hi, sb, ts, g2, e2);
         }
     }
 }
@@ -217,30 +193,7 @@ k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uin
         quant1d_blocks<T, kSR, kNoise>(x, ld, blocks, bpr, cols, ts, seed, codes, scales,
                                        blockIdx.x * kThreads * kQUnroll + threadIdx.x, g2, e2);
     }
-    if constexpr (kNoise) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            g2 += __shfl_xor(g2, off);
-            e2 += __shfl_xor(e2, off);
-        }
-        __shared__ double part[2][kThreads / 64];
-        if ((threadIdx.x & 63) == 0) {
-            part[0][threadIdx.x >> 6] = g2;
-            part[1][threadIdx.x >> 6] = e2;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            double a = 0.0, c = 0.0;
-#pragma unroll
-            for (int w = 0; w < kThreads / 64; ++w) {
-                a += part[0][w];
-                c += part[1][w];
-            }
-            const double inv = 1.0 / ((double)ts.s_enc * (double)ts.s_enc);
-            atomicAdd(sums, a * inv);
-            atomicAdd(sums + 1, c * inv);
-        }
-    }
+    if constexpr (kNoise) publish_noise<kThreads>(g2, e2, ts, sums);
 }
 
 __global__ void k_fill_f64x2(double* p) {

@@ -106,6 +106,17 @@ def test_amax_accumulate_validation(L):
     assert L.nvfp4_hadamard_amax_accumulate(FAKE, nv.BF16, 32, 16, 16, 1, FAKE + 2, None) == nv.ERR_ALIGN
 
 
+def test_hadamard_noise_validation(L):
+    q = _q(16, 32)                               # out [F=16 x T=32]
+    assert L.nvfp4_hadamard_quantize_noise(FAKE, nv.BF16, 16, 1, None, nv.SR, 0, C.byref(q), None,
+                                           None) == nv.ERR_NULL
+    assert L.nvfp4_hadamard_quantize_noise(FAKE, nv.BF16, 16, 1, None, nv.SR, 0, C.byref(q),
+                                           FAKE + 4, None) == nv.ERR_ALIGN
+    bad = _q(12, 32)                             # F = 12 features: not a multiple of 8
+    assert L.nvfp4_hadamard_quantize_noise(FAKE, nv.BF16, 16, 1, None, nv.SR, 0, C.byref(bad),
+                                           FAKE, None) == nv.ERR_SHAPE
+
+
 def test_gemm_validation(L):
     a, b = _q(64, 64), _q(32, 48)
     assert L.nvfp4_gemm(C.byref(a), C.byref(b), FAKE, nv.F32, 32, None) == nv.ERR_SHAPE

@@ -76,3 +76,34 @@ def test_noise_full_size_dgrad_operand(nv, orc):
     got, ref = _check(nv, orc, x, 1, W.CFG3["sr_seed"])
     rep = nv.noise_report(torch.tensor(got))
     assert rep["ratio"] == pytest.approx((ref[0] / ref[1]) ** 0.5, rel=1e-5)
+
+
+def _check_rht(nv, orc, x, rounding, seed, sign_seed):
+    """The Hadamard quantizer's noise sums against the oracle's on the transformed tensor."""
+    q, sums = nv.hadamard_quantize_noise(x.to(DEV), sign_seed, rounding, seed)
+    torch.cuda.synchronize()
+    xb = W.bits(x)
+    o = orc.hadamard_quantize(xb, sign_seed, rounding=rounding, seed=seed)
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), o["codes"])
+    np.testing.assert_array_equal(q.scales.cpu().numpy(), o["scales"])
+    g2, e2 = orc.quant_noise(orc.hadamard_transform(xb, sign_seed), o)
+    got = sums.cpu().numpy()
+    assert abs(got[0] - g2) <= REL * g2, (got, g2)
+    assert abs(got[1] - e2) <= REL * e2, (got, e2)
+    return got, (g2, e2)
+
+
+@pytest.mark.parametrize("rounding", [0, 1])
+@pytest.mark.parametrize("T,F", [(64, 24), (512, 64), (528, 136)])
+def test_hadamard_noise_small(nv, orc, rounding, T, F):
+    _check_rht(nv, orc, W.grad((T, F), T + F), rounding, 0x99, 0x51E4)
+
+
+def test_hadamard_noise_full_size_wgrad_operand(nv, orc):
+    """dY 16384 x 4096 through the Hadamard quantizer with SR at the wgrad seeds (the capped
+    grid takes two chunk blocks per workgroup here): whole-tensor sums against the oracle, and
+    the transformed tensor's squared norm equals the input's to rounding (orthogonal transform)."""
+    x = W.grad((16384, 4096), W.CFG4["seeds"][1])
+    got, ref = _check_rht(nv, orc, x, 1, W.CFG4["sr_seed"], W.CFG4["sign_seed"])
+    xv = orc.values(W.bits(x))
+    assert got[0] == pytest.approx(float(np.sum(xv * xv)), rel=1e-5)
