@@ -290,22 +290,49 @@ struct MxDma2 {
     }
 };
 
-// The fragments of sub-step s (K-block q = 2s + lane / 32 of each row).
+// The fragments of sub-step s (K-block q = 2s + lane / 32 of each row).  The scales stay in
+// registers for the whole step: at s = 0 a lane reads its rows' two scale words (blocks 0-3 and
+// 4-7) and keeps the four bytes of its half, blocks h, 2 + h, 4 + h, 6 + h (h = lane / 32), in
+// one word (one v_perm), so that sub-step s finds its block in byte s for both halves and the
+// MFMA selects it with op_sel = s (no per-sub-step scale read or byte extract).  At s = 1 the
+// words are copied from the other fragment set `prev`, which holds sub-step 0 of the same step;
+// at s = 2 and 3 the set still holds this step's words from s = 0 or 1.
 template <int TM, int TN>
-__device__ __forceinline__ void d2_read_frags(const MxStage2& st, MxFrags<TM, TN>& f, int wm, int wn,
+__device__ __forceinline__ void d2_read_frags(const MxStage2& st, MxFrags<TM, TN>& f,
+                                              const MxFrags<TM, TN>& prev, int wm, int wn,
                                               int lane, int s) {
-    const int lrow = lane & 31, q = 2 * s + (lane >> 5), sh = 8 * (q & 3), wsel = s >> 1;
+    const int lrow = lane & 31, q = 2 * s + (lane >> 5);
+    const uint32_t sel = (lane >> 5) ? 0x07050301u : 0x06040200u;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int r = wm * TM * 32 + i * 32 + lrow;
         f.a[i] = st.a[r * 8 + d2_swz(r, q)];
-        f.ea[i] = (st.sa[wsel][r] >> sh) & 0xFFu;
+        if (s == 0) f.ea[i] = __builtin_amdgcn_perm(st.sa[1][r], st.sa[0][r], sel);
+        if (s == 1) f.ea[i] = prev.ea[i];
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int r = wn * TN * 32 + j * 32 + lrow;
         f.b[j] = st.b[r * 8 + d2_swz(r, q)];
-        f.eb[j] = (st.sb[wsel][r] >> sh) & 0xFFu;
+        if (s == 0) f.eb[j] = __builtin_amdgcn_perm(st.sb[1][r], st.sb[0][r], sel);
+        if (s == 1) f.eb[j] = prev.eb[j];
+    }
+}
+
+// mx_mfma with the scale byte chosen by op_sel: byte SEL of each scale word.
+template <int TM, int TN, bool kT, int SEL>
+__device__ __forceinline__ void mx_mfma_sel(const MxFrags<TM, TN>& f, float16v (&acc)[TM][TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int8v va = fp4_operand(f.a[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int8v vb = fp4_operand(f.b[j]);
+            acc[i][j] = kT ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                 vb, va, acc[i][j], kFmtFp4, kFmtFp4, SEL, (int)f.eb[j], SEL, (int)f.ea[i])
+                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                 va, vb, acc[i][j], kFmtFp4, kFmtFp4, SEL, (int)f.ea[i], SEL, (int)f.eb[j]);
+        }
     }
 }
 
@@ -339,36 +366,36 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
     dma.issue(0, lds0, wave);
     MxFrags<TM, TN> f0, f1;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) { f1.a[i] = make_uint4(0, 0, 0, 0); f1.ea[i] = 127; }
+    for (int i = 0; i < TM; ++i) { f1.a[i] = make_uint4(0, 0, 0, 0); f1.ea[i] = 0x7F7F7F7Fu; }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) { f1.b[j] = make_uint4(0, 0, 0, 0); f1.eb[j] = 127; }
+    for (int j = 0; j < TN; ++j) { f1.b[j] = make_uint4(0, 0, 0, 0); f1.eb[j] = 0x7F7F7F7Fu; }
     wait_vmcnt<0>();
     lds_barrier();
     dma.issue(1, lds0 + sizeof(MxStage2), wave);
-    d2_read_frags<TM, TN>(st[0], f0, wm, wn, lane, 0);
+    d2_read_frags<TM, TN>(st[0], f0, f1, wm, wn, lane, 0);
     // Step kt multiplies stage kt % 2 while step kt + 1 lands in the other; after the barrier
     // that ends step kt (all reads of its stage done) step kt + 2 is fetched into it.
     int cs = 0;
     for (int kt = 0; kt < nk; ++kt) {
         const MxStage2& cur = st[cs];
-        mx_mfma<TM, TN, kT>(f1, acc);                   // previous step, sub-step 3
+        mx_mfma_sel<TM, TN, kT, 3>(f1, acc);            // previous step, sub-step 3
         __builtin_amdgcn_sched_barrier(0);
-        d2_read_frags<TM, TN>(cur, f1, wm, wn, lane, 1);
-        mx_mfma<TM, TN, kT>(f0, acc);                   // sub-step 0
+        d2_read_frags<TM, TN>(cur, f1, f0, wm, wn, lane, 1);
+        mx_mfma_sel<TM, TN, kT, 0>(f0, acc);            // sub-step 0
         __builtin_amdgcn_sched_barrier(0);
-        d2_read_frags<TM, TN>(cur, f0, wm, wn, lane, 2);
-        mx_mfma<TM, TN, kT>(f1, acc);                   // sub-step 1
+        d2_read_frags<TM, TN>(cur, f0, f1, wm, wn, lane, 2);
+        mx_mfma_sel<TM, TN, kT, 1>(f1, acc);            // sub-step 1
         __builtin_amdgcn_sched_barrier(0);
-        d2_read_frags<TM, TN>(cur, f1, wm, wn, lane, 3);
-        mx_mfma<TM, TN, kT>(f0, acc);                   // sub-step 2
+        d2_read_frags<TM, TN>(cur, f1, f0, wm, wn, lane, 3);
+        mx_mfma_sel<TM, TN, kT, 2>(f0, acc);            // sub-step 2
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                                // step kt + 1 has landed
         lds_barrier();
         dma.issue(kt + 2, lds0 + cs * (uint32_t)sizeof(MxStage2), wave);
         cs ^= 1;
-        d2_read_frags<TM, TN>(st[cs], f0, wm, wn, lane, 0);
+        d2_read_frags<TM, TN>(st[cs], f0, f1, wm, wn, lane, 0);
     }
-    mx_mfma<TM, TN, kT>(f1, acc);                       // sub-step 3 of the last step
+    mx_mfma_sel<TM, TN, kT, 3>(f1, acc);                // sub-step 3 of the last step
     wait_vmcnt<0>();                                    // the clamped re-fetches past the end
 
     const int64_t r0 = m0 + wm * TM * 32, c0 = n0 + wn * TN * 32;
