@@ -39,6 +39,15 @@ template <> struct Tile16x8<uint16_t> {
         const uint32_t v = f < 2 ? w[i].x : f < 4 ? w[i].y : f < 6 ? w[i].z : w[i].w;
         return (f & 1) ? bf16_hi(v) : bf16_lo(v);
     }
+    // Row i times d_i (bit i of sign_mask set: d_i = -1), on the packed words: one xor per two
+    // elements, bit-identical to negating each unpacked value.
+    __device__ __forceinline__ void apply_signs(uint32_t sign_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t s = ((sign_mask >> i) & 1u) ? 0x80008000u : 0u;
+            w[i].x ^= s; w[i].y ^= s; w[i].z ^= s; w[i].w ^= s;
+        }
+    }
 };
 
 template <> struct Tile16x8<float> {
@@ -54,6 +63,15 @@ template <> struct Tile16x8<float> {
         const float4& v = f < 4 ? a[i] : b[i];
         const int g = f & 3;
         return g == 0 ? v.x : g == 1 ? v.y : g == 2 ? v.z : v.w;
+    }
+    __device__ __forceinline__ void apply_signs(uint32_t sign_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t s = ((sign_mask >> i) & 1u) << 31;
+            float* e[8] = {&a[i].x, &a[i].y, &a[i].z, &a[i].w, &b[i].x, &b[i].y, &b[i].z, &b[i].w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) *e[k] = __uint_as_float(__float_as_uint(*e[k]) ^ s);
+        }
     }
 };
 
@@ -116,11 +134,10 @@ __device__ __forceinline__ float hd16_absmax(float* v, const RhtPlan& p) {
     return m;
 }
 
-// In place: v <- (1/4) H16 D v with D applied first and butterflies in the order h = 1, 2, 4, 8.
-__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
-    sign_mask = __builtin_amdgcn_readfirstlane(sign_mask);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
+// In place: v <- (1/4) H16 v, butterflies in the order h = 1, 2, 4, 8 then one multiply by 1/4
+// each.  The random signs D are applied before, to the loaded tile (apply_signs), so that the
+// whole is (1/4) H16 D x with D applied first.
+__device__ __forceinline__ void h16_quarter(float* v) {
 #pragma unroll
     for (int hs = 1; hs < 16; hs <<= 1)
 #pragma unroll
@@ -275,12 +292,14 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
     uint64_t idx = (uint64_t)rc.f0 * (uint64_t)Tn + (uint64_t)rc.c * 16;    // SR element index
     uint8_t* cp = codes + rc.f0 * (Tn / 2) + rc.c * 8;
     uint8_t* sp = scales + rc.f0 * (Tn / 16) + rc.c;
+    Tile16x8<T> sgn = tile;
+    sgn.apply_signs(__builtin_amdgcn_readfirstlane(mask));     // the same in every lane
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
         float v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
-        rht16(v, mask);
+        for (int i = 0; i < 16; ++i) v[i] = sgn.get(i, f);
+        h16_quarter(v);
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
