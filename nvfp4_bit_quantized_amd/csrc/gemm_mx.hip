@@ -148,8 +148,9 @@ __device__ __forceinline__ void mx_read_frags(const MxStage& st, MxFrags<TM, TN>
 }
 
 // kT: B is the MFMA's first operand and each accumulator tile is held transposed (the layout
-// the staged bf16 epilogue takes); otherwise one output column per lane.
-template <int TM, int TN, bool kT>
+// the staged bf16 epilogue takes); otherwise one output column per lane.  The E8M0 scale of each
+// operand is byte SEL of its scale word (the MFMA's op_sel).
+template <int TM, int TN, bool kT, int SEL = 0>
 __device__ __forceinline__ void mx_mfma(const MxFrags<TM, TN>& f, float16v (&acc)[TM][TN]) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -158,9 +159,9 @@ __device__ __forceinline__ void mx_mfma(const MxFrags<TM, TN>& f, float16v (&acc
         for (int j = 0; j < TN; ++j) {
             const int8v vb = fp4_operand(f.b[j]);
             acc[i][j] = kT ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                 vb, va, acc[i][j], kFmtFp4, kFmtFp4, 0, (int)f.eb[j], 0, (int)f.ea[i])
+                                 vb, va, acc[i][j], kFmtFp4, kFmtFp4, SEL, (int)f.eb[j], SEL, (int)f.ea[i])
                            : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                 va, vb, acc[i][j], kFmtFp4, kFmtFp4, 0, (int)f.ea[i], 0, (int)f.eb[j]);
+                                 va, vb, acc[i][j], kFmtFp4, kFmtFp4, SEL, (int)f.ea[i], SEL, (int)f.eb[j]);
         }
     }
 }
@@ -319,23 +320,6 @@ __device__ __forceinline__ void d2_read_frags(const MxStage2& st, MxFrags<TM, TN
     }
 }
 
-// mx_mfma with the scale byte chosen by op_sel: byte SEL of each scale word.
-template <int TM, int TN, bool kT, int SEL>
-__device__ __forceinline__ void mx_mfma_sel(const MxFrags<TM, TN>& f, float16v (&acc)[TM][TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int8v va = fp4_operand(f.a[i]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int8v vb = fp4_operand(f.b[j]);
-            acc[i][j] = kT ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                 vb, va, acc[i][j], kFmtFp4, kFmtFp4, SEL, (int)f.eb[j], SEL, (int)f.ea[i])
-                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                 va, vb, acc[i][j], kFmtFp4, kFmtFp4, SEL, (int)f.ea[i], SEL, (int)f.eb[j]);
-        }
-    }
-}
-
 template <int WM, int WN, int TM, int TN, bool kBF16Out>
 __global__ void __launch_bounds__(kMxThreads)
 k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict__ C, int64_t ldc) {
@@ -378,16 +362,16 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
     int cs = 0;
     for (int kt = 0; kt < nk; ++kt) {
         const MxStage2& cur = st[cs];
-        mx_mfma_sel<TM, TN, kT, 3>(f1, acc);            // previous step, sub-step 3
+        mx_mfma<TM, TN, kT, 3>(f1, acc);                // previous step, sub-step 3
         __builtin_amdgcn_sched_barrier(0);
         d2_read_frags<TM, TN>(cur, f1, f0, wm, wn, lane, 1);
-        mx_mfma_sel<TM, TN, kT, 0>(f0, acc);            // sub-step 0
+        mx_mfma<TM, TN, kT, 0>(f0, acc);                // sub-step 0
         __builtin_amdgcn_sched_barrier(0);
         d2_read_frags<TM, TN>(cur, f0, f1, wm, wn, lane, 2);
-        mx_mfma_sel<TM, TN, kT, 1>(f1, acc);            // sub-step 1
+        mx_mfma<TM, TN, kT, 1>(f1, acc);                // sub-step 1
         __builtin_amdgcn_sched_barrier(0);
         d2_read_frags<TM, TN>(cur, f1, f0, wm, wn, lane, 3);
-        mx_mfma_sel<TM, TN, kT, 2>(f0, acc);            // sub-step 2
+        mx_mfma<TM, TN, kT, 2>(f0, acc);                // sub-step 2
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                                // step kt + 1 has landed
         lds_barrier();
@@ -395,7 +379,7 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
         cs ^= 1;
         d2_read_frags<TM, TN>(st[cs], f0, f1, wm, wn, lane, 0);
     }
-    mx_mfma_sel<TM, TN, kT, 3>(f1, acc);                // sub-step 3 of the last step
+    mx_mfma<TM, TN, kT, 3>(f1, acc);                    // sub-step 3 of the last step
     wait_vmcnt<0>();                                    // the clamped re-fetches past the end
 
     const int64_t r0 = m0 + wm * TM * 32, c0 = n0 + wn * TN * 32;
