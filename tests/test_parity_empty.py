@@ -49,6 +49,8 @@ def test_empty_quantizers(nv, dtype):
         assert _scalars(nv.hadamard_quantize(e_tok, 7, rnd, 3)) == (0.0, 1.0)
         r, t = nv.quantize_dual(e_tok, 7, rnd, 3, 4)
         assert _scalars(r) == (0.0, 1.0) and _scalars(t) == (0.0, 1.0)
+        qn, sums = nv.hadamard_quantize_noise(e_tok, 7, rnd, 3)
+        assert _scalars(qn) == (0.0, 1.0) and sums.cpu().tolist() == [0.0, 0.0]
     nv.mx_quantize_1d_t(torch.empty((0, 32), dtype=dtype, device=DEV))
     torch.cuda.synchronize()
 
