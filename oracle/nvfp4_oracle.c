@@ -18,10 +18,13 @@
  * Where the pages are silent the reading taken is named in the comment ("reading: ...").
  *
  * Parity unpinned (no page value or closed form fixes them; the GPU only has to agree):
- *   - the fp32 operation order of the tensor/block scale (or_tensor_scales, block scale step);
- *   - the butterfly order of the 16-point Hadamard transform (its matrix IS pinned);
- *   - the mapping of Philox output bits to stochastic-rounding uniforms and to Hadamard signs
- *     (only their statistics and the generator itself are pinned).
+ *   - the fp32 operation order of the block scale step (t = amax_b * k1, enc = s_enc / scale);
+ *     the tensor scales themselves ARE pinned as single correctly rounded divisions;
+ *   - the butterfly order of the 16-point Hadamard transform (its matrix IS pinned).
+ * The Philox generator is pinned by its published known answers, and the two maps that draw
+ * from it are pinned by the properties a random draw must have (balanced, pairwise independent
+ * Hadamard signs; an injective, pairwise independent element -> SR draw map).  WHICH output
+ * bits each map takes is a convention with no observable consequence beyond those properties.
  */
 #include <stdint.h>
 #include <stddef.h>
