@@ -32,6 +32,10 @@
  *   - Inputs must be finite; for NaN/Inf inputs the outputs are unspecified.
  *   - Row strides `ld` are in elements, ld >= cols, and ld * element size must be a multiple of
  *     16 bytes.  Quantized buffers are dense (no stride).
+ *   - Size limit of every row-wise call (amax, quantizers, dequantize, sweep): rows * cols / 8
+ *     < 2^31, i.e. fewer than 2^34 elements (NVFP4_ERR_SHAPE beyond).  The token-major calls
+ *     (Hadamard, dual, transposing MXFP4) take T <= 33553920 tokens (T / 512 <= 65535
+ *     workgroup rows) and F < 2^31 features.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -93,12 +97,15 @@ typedef struct {
 NVFP4_API const char *nvfp4_status_string(nvfp4_status s);
 
 /* Per-tensor amax: *amax_out = max |x| over x [rows x cols] (row stride ld).  This is the first
- * level of the two-level scaling [P3 Come funziona NVFP4?].  amax_out is overwritten. */
+ * level of the two-level scaling [P3 Come funziona NVFP4?].  amax_out is overwritten.
+ * cols % 8 == 0 (the pass reads 8 elements at a time), else NVFP4_ERR_SHAPE; every NVFP4
+ * tensor satisfies it (cols % 16 == 0). */
 NVFP4_API nvfp4_status nvfp4_amax(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                                   float *amax_out, void *stream);
 
 /* amax of the random-Hadamard-transformed tensor (see nvfp4_hadamard_quantize), without
- * writing the transform: x is [T tokens x F features], T % 16 == 0. */
+ * writing the transform: x is [T tokens x F features], T % 16 == 0 and F % 8 == 0 (else
+ * NVFP4_ERR_SHAPE). */
 NVFP4_API nvfp4_status nvfp4_hadamard_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
                                            uint64_t sign_seed, float *amax_out, void *stream);
 
@@ -108,7 +115,8 @@ NVFP4_API nvfp4_status nvfp4_hadamard_amax(const void *x, nvfp4_dtype dt, int64_
  * amax of x alone), which lets one amax cover several tensors or micro-batches and lets a caller
  * clear many amax slots in one operation instead of one launch per slot.  *amax_inout must hold
  * a non-negative, non-NaN float (it is raised by an unsigned atomic max on its bit pattern).  An
- * empty x leaves it unchanged.  Same shape rules and errors as the non-accumulating calls. */
+ * empty x leaves it unchanged.  Same shape rules and errors as the non-accumulating calls:
+ * cols % 8 == 0 for nvfp4_amax_accumulate, T % 16 == 0 and F % 8 == 0 for the Hadamard form. */
 NVFP4_API nvfp4_status nvfp4_amax_accumulate(const void *x, nvfp4_dtype dt, int64_t rows, int64_t cols,
                                              int64_t ld, float *amax_inout, void *stream);
 NVFP4_API nvfp4_status nvfp4_hadamard_amax_accumulate(const void *x, nvfp4_dtype dt, int64_t T, int64_t F,
@@ -153,6 +161,7 @@ NVFP4_API nvfp4_status nvfp4_quantize_2d(const void *w, nvfp4_dtype dt, int64_t 
  * Philox4x32-10(key = sign_seed, counter = 0) is set.  The result is written feature-major:
  * out is [F x T] (out->rows = F, out->cols = T, layout NVFP4_BLK_1x16), so the token dimension
  * is the contiguous K of the wgrad GEMM and each 16-token chunk is one NVFP4 block.
+ * T % 16 == 0 and F % 8 == 0 (a thread transforms 8 adjacent features), else NVFP4_ERR_SHAPE.
  * amax_in: the amax of the TRANSFORMED tensor, or NULL to compute it. */
 NVFP4_API nvfp4_status nvfp4_hadamard_quantize(const void *x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,
                                                const float *amax_in, nvfp4_round rnd, uint64_t seed,
@@ -166,7 +175,7 @@ NVFP4_API nvfp4_status nvfp4_hadamard_quantize(const void *x, nvfp4_dtype dt, in
  * equals sum x^2 up to rounding.  sums: device, two doubles, 8-byte aligned, overwritten.
  * Accumulated as in nvfp4_quantize_1d_noise (fp32 per 16-element block on values times s_enc,
  * fp64 across blocks, device atomics: the last bits vary from run to run); codes and scales are
- * exactly those of nvfp4_hadamard_quantize. */
+ * exactly those of nvfp4_hadamard_quantize.  Shape rules as nvfp4_hadamard_quantize. */
 NVFP4_API nvfp4_status nvfp4_hadamard_quantize_noise(const void *x, nvfp4_dtype dt, int64_t ld,
                                                      uint64_t sign_seed, const float *amax_in,
                                                      nvfp4_round rnd, uint64_t seed,

@@ -18,6 +18,10 @@ forward pass rounds to nearest, backward and update passes round stochastically)
 Every one of these steps runs in the HIP library; this file only allocates outputs and passes
 pointers.  Shapes: T, in and out multiples of 16.
 
+dW comes back in the weight's dtype, as autograd requires: for fp32 (master) weights it is the
+wgrad GEMM's fp32 accumulation as is; for bf16 weights the GEMM rounds that fp32 result once to
+bf16 (round to nearest even) on output.
+
 The MXFP4 comparison format ("I ricercatori di Nvidia ...", NVFP4 in pratica: MXFP4 needed more
 training data to match NVFP4) runs the same three GEMMs with every operand in MXFP4 (32-element
 blocks, power-of-two scales applied by the matrix core), the same rounding per pass, and plain

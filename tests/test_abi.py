@@ -93,6 +93,21 @@ def test_quantize_2d_and_hadamard_validation(L):
     assert L.nvfp4_amax(FAKE, nv.BF16, 4, 16, 16, FAKE + 1, None) == nv.ERR_ALIGN
 
 
+def test_documented_multiple_of_8_rules(L):
+    """nvfp4_amax needs cols % 8 == 0 and every Hadamard call F % 8 == 0 (with T % 16 == 0 met),
+    as include/nvfp4.h states; each violation alone gives NVFP4_ERR_SHAPE."""
+    for cols in (4, 12, 20):
+        assert L.nvfp4_amax(FAKE, nv.BF16, 4, cols, 32, FAKE, None) == nv.ERR_SHAPE
+        assert L.nvfp4_amax_accumulate(FAKE, nv.BF16, 4, cols, 32, FAKE, None) == nv.ERR_SHAPE
+    for F in (4, 12, 20):
+        assert L.nvfp4_hadamard_amax(FAKE, nv.BF16, 32, F, 32, 1, FAKE, None) == nv.ERR_SHAPE
+        assert L.nvfp4_hadamard_amax_accumulate(FAKE, nv.BF16, 32, F, 32, 1, FAKE, None) == nv.ERR_SHAPE
+        q = _q(F, 32)                            # out [F x T=32]: T is fine, F is not
+        assert L.nvfp4_hadamard_quantize(FAKE, nv.BF16, 32, 1, None, nv.RNE, 0, C.byref(q), None) == nv.ERR_SHAPE
+        assert L.nvfp4_hadamard_quantize_noise(FAKE, nv.BF16, 32, 1, None, nv.SR, 0, C.byref(q), FAKE,
+                                               None) == nv.ERR_SHAPE
+
+
 def test_amax_accumulate_validation(L):
     """The accumulating amax calls validate like the plain ones (nothing is enqueued)."""
     assert L.nvfp4_amax_accumulate(None, nv.BF16, 4, 16, 16, FAKE, None) == nv.ERR_NULL
