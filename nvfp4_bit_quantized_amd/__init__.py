@@ -189,7 +189,7 @@ def quantize_1d_noise(x: torch.Tensor, rounding: int = SR, seed: int = 0,
                       amax_in: torch.Tensor | None = None, out: QTensor | None = None,
                       sums: torch.Tensor | None = None):
     """quantize_1d plus the noise diagnostic: (QTensor, sums) with sums a device float64 [2] =
-    (sum x^2, sum (Q(x) - x)^2).  ``noise_report(sums)`` turns it into norms and the ratio."""
+    (sum x^2, sum (Q(x) - x)^2).  ``diagnostics.noise_report(sums)`` reads them on the host."""
     x, dt, ld = _x(x)
     q = QTensor.empty(x.shape[0], x.shape[1], BLK_1x16, x.device) if out is None else out
     sums = torch.empty(2, dtype=torch.float64, device=x.device) if sums is None else sums
@@ -215,15 +215,6 @@ def qdq(x: torch.Tensor, block: int, scale_fmt: int, rounding: int = RNE, seed: 
                                         _ptr(amax_in), rounding, seed, _ptr(y), y.stride(0),
                                         _ptr(amax_out), _ptr(sums), _stream(x.device)))
     return y, amax_out, sums
-
-
-def noise_report(sums: torch.Tensor) -> dict:
-    """Norms and ratio from the two sums: quantized training is flagged as inefficient when
-    ||g|| < sqrt(3) * ||Q(g) - g||."""
-    g2, e2 = (float(v) for v in sums.cpu().tolist())
-    g, e = g2 ** 0.5, e2 ** 0.5
-    ratio = g / e if e > 0 else float("inf")
-    return {"grad_norm": g, "noise_norm": e, "ratio": ratio, "below_sqrt3": ratio < 3 ** 0.5}
 
 
 def quantize_2d(w: torch.Tensor, transposed: bool = True, amax_in: torch.Tensor | None = None,

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import workloads as W
+from gemm_check import assert_gemm_close
 
 pytestmark = pytest.mark.gpu
 
@@ -100,4 +101,4 @@ def test_edge_gemm(nv, orc, kind):
     if den == 0.0:
         assert not got.any()
     else:
-        assert np.linalg.norm(got - ref) / den <= 1e-5
+        assert_gemm_close(got, ref, "edge gemm")

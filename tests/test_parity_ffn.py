@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import workloads as W
+from gemm_check import assert_gemm_close
 
 pytestmark = pytest.mark.gpu
 
@@ -38,10 +39,6 @@ def _host_q(q):
         d["s_dec"] = float(q.s_dec.item())
         d["amax"] = float(q.amax.item())
     return d
-
-
-def _rel_l2(a, b):
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
 def test_ffn_1d_quantizers_sampled(nv, orc):
@@ -134,7 +131,7 @@ def test_ffn_gemm_sampled(nv, orc, ffn_operands, name, a, b, dt):
     rows = _rows(M, 32, [g[0] for g in GEMMS].index(name) + 11)
     ref = orc.gemm_f64(_host_q(qa), _host_q(qb), M, N, K, rows=rows)
     got = c[torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
-    assert _rel_l2(got, ref) <= 1e-5
+    assert_gemm_close(got, ref, name)
     if dt == torch.bfloat16:
         cb = nv.gemm(qa, qb, torch.bfloat16)
         torch.cuda.synchronize()
@@ -148,4 +145,4 @@ def test_ffn_mxfp4_gemm_sampled(nv, orc, ffn_operands):
     rows = _rows(M, 32, 5)
     ref = orc.mx_gemm_f64(_host_q(qa), _host_q(qb), M, N, K, rows=rows)
     got = c[torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
-    assert _rel_l2(got, ref) <= 1e-5
+    assert_gemm_close(got, ref, "mxfp4 up fprop")

@@ -11,6 +11,8 @@ import pytest
 import torch
 
 import workloads as W
+from gemm_check import assert_gemm_close
+from nvfp4_bit_quantized_amd.diagnostics import noise_report as _noise_report
 
 pytestmark = pytest.mark.gpu
 
@@ -25,11 +27,6 @@ def L():
     m.lib()
     from nvfp4_bit_quantized_amd import linear
     return linear
-
-
-def _rel(a, b):
-    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
 def _t(q):
@@ -55,9 +52,9 @@ def test_linear_matches_oracle(L, orc, T, fin, fout):
     y_ref = orc.gemm_f64(ox, ow, T, fout, fin)
     dx_ref = orc.gemm_f64(ody, _t(ow), T, fin, fout)
     dw_ref = orc.gemm_f64(odyt, oxt, fout, fin, T)
-    assert _rel(y.detach().cpu().numpy(), y_ref) <= 1e-5
-    assert _rel(xd.grad.cpu().numpy(), dx_ref) <= 1e-5
-    assert _rel(wd.grad.cpu().numpy(), dw_ref) <= 1e-5
+    assert_gemm_close(y.detach().cpu().numpy(), y_ref, "y")
+    assert_gemm_close(xd.grad.cpu().numpy(), dx_ref, "dx")
+    assert_gemm_close(wd.grad.cpu().numpy(), dw_ref, "dw")
 
 
 @pytest.mark.parametrize("T,fin,fout", [(64, 128, 96), (256, 96, 64)])
@@ -79,9 +76,9 @@ def test_mx_linear_matches_oracle(L, orc, T, fin, fout):
                              T, fin, fout)
     dw_ref = orc.mx_gemm_f64(orc.mx_quantize_1d(tr(dyb), 1, sw), orc.mx_quantize_1d(tr(xb)),
                              fout, fin, T)
-    assert _rel(y.detach().cpu().numpy(), y_ref) <= 1e-5
-    assert _rel(xd.grad.cpu().numpy(), dx_ref) <= 1e-5
-    assert _rel(wd.grad.cpu().numpy(), dw_ref) <= 1e-5
+    assert_gemm_close(y.detach().cpu().numpy(), y_ref, "y")
+    assert_gemm_close(xd.grad.cpu().numpy(), dx_ref, "dx")
+    assert_gemm_close(wd.grad.cpu().numpy(), dw_ref, "dw")
 
 
 def test_mx_module_shapes(L):
@@ -155,8 +152,8 @@ def test_ffn_pair_against_bf16(L):
     w1 = W.weight((ff, d), 602).to(DEV)
     w2 = W.weight((d, ff), 603).to(DEV)
     dy = W.grad((T, d), 604).to(DEV)
-    e_x = 1.0 / nvm.noise_report(nvm.quantize_1d_noise(x, nvm.RNE)[1])["ratio"]
-    e_dy = 1.0 / nvm.noise_report(nvm.quantize_1d_noise(dy, nvm.SR, 7)[1])["ratio"]
+    e_x = 1.0 / _noise_report(nvm.quantize_1d_noise(x, nvm.RNE)[1])["ratio"]
+    e_dy = 1.0 / _noise_report(nvm.quantize_1d_noise(dy, nvm.SR, 7)[1])["ratio"]
     e = max(e_x, e_dy)
     ref = _ffn_step(*_ffn(L, d, ff, True, w1, w2, 1), x, dy)
     up, down = _ffn(L, d, ff, False, w1, w2, 1)

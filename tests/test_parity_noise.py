@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import workloads as W
+from nvfp4_bit_quantized_amd.diagnostics import noise_report as _noise_report
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +75,7 @@ def test_noise_full_size_dgrad_operand(nv, orc):
     """dY 8192 x 4096 with SR at the dgrad seed: whole-tensor sums against the oracle."""
     x = W.grad((8192, 4096), W.CFG3["seed"])
     got, ref = _check(nv, orc, x, 1, W.CFG3["sr_seed"])
-    rep = nv.noise_report(torch.tensor(got))
+    rep = _noise_report(torch.tensor(got))
     assert rep["ratio"] == pytest.approx((ref[0] / ref[1]) ** 0.5, rel=1e-5)
 
 

@@ -183,3 +183,26 @@ def test_full_wgrad_operands(nv, orc):
     dy = W.grad(c["dy"], c["seeds"][1])
     g = nv.hadamard_quantize(dy.to(DEV), c["sign_seed"], rounding=1, seed=c["sr_seed"])
     _same_q(g, orc.hadamard_quantize(W.bits(dy), c["sign_seed"], rounding=1, seed=c["sr_seed"]), "dY rht SR")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_full_dequantize(nv, orc, dtype):
+    """Dequantize at full size, bit-exact: X 8192x4096 (1D, its codes equal the oracle's, as
+    test_full_fprop_operands shows) and W 4096x4096 (16x16 tiles) to fp32 and to bf16."""
+    for make, shape, seed, two_d in ((W.act, W.CFG2["x"], W.CFG2["seeds"][0], False),
+                                     (W.weight, W.CFG2["w"], W.CFG2["seeds"][1], True)):
+        x = make(shape, seed)
+        if two_d:
+            g, _ = nv.quantize_2d(x.to(DEV), transposed=False)
+            o = orc.quantize_2d(W.bits(x), transposed=False)
+        else:
+            g = nv.quantize_1d(x.to(DEV))
+            o = orc.quantize_1d(W.bits(x))
+        _same_q(g, o, f"dequant operand {shape}")
+        y = nv.dequantize(g, dtype)
+        ref = orc.dequantize(o, *shape, out_bf16=(dtype == torch.bfloat16))
+        torch.cuda.synchronize()
+        got = y.cpu().view(torch.int16).numpy().view(np.uint16) if dtype == torch.bfloat16 \
+            else y.cpu().numpy()
+        np.testing.assert_array_equal(got, ref, err_msg=f"dequantize {shape} {dtype}")
+        del x, g, y

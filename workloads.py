@@ -128,4 +128,7 @@ CFG3 = dict(dy=(8192, 4096), seed=301, sr_seed=SR_SEED_DGRAD)
 CFG4 = dict(x=(16384, 4096), dy=(16384, 4096), seeds=(401, 402), sign_seed=SIGN_SEED_WGRAD,
             sr_seed=SR_SEED_WGRAD)
 # cfg5: FFN pair up 5120->20480, down 20480->5120, 16384 tokens (seeds 501..506)
-CFG5 = dict(tokens=16384, d_model=5120, d_ff=20480, seeds=(501, 502, 503, 504, 505, 506))
+CFG5 = dict(tokens=16384, d_model=5120, d_ff=20480, seeds=(501, 502, 503, 504, 505, 506),
+            # per layer: Hadamard sign seed, SR seed of the dgrad operand, SR seed of the wgrad one
+            layer_seeds={"up": (0x51E40051, 0x5EED0051, 0x5EED0052),
+                         "down": (0x51E40052, 0x5EED0053, 0x5EED0054)})
