@@ -40,6 +40,7 @@
 #ifndef NVFP4_H
 #define NVFP4_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 /* Only the functions declared here are exported from the library; everything else it
@@ -220,6 +221,27 @@ NVFP4_API nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, nvfp4_dt
  * K == 0 writes zeros (the empty sum) and reads neither operand's codes nor scales. */
 NVFP4_API nvfp4_status nvfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                                   int64_t ldc, void *stream);
+
+/* Bytes of workspace with which nvfp4_gemm_ws splits an M x N x K GEMM on the current device
+ * (see there); 0 when it would not split (the last round of 256 x 256 output tiles over the
+ * device's compute units is empty or more than half full, K % 64 != 0, or K too short for
+ * splits of at least 16 steps of 64).  At most 64 MiB (256 partial tiles of 256 KiB).  Negative
+ * or >= 2^31 dimensions: NVFP4_ERR_SHAPE; bytes NULL: NVFP4_ERR_NULL. */
+NVFP4_API nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, size_t *bytes);
+
+/* nvfp4_gemm with a caller-owned device workspace [P2 Describir: all three GEMMs on FP4
+ * operands].  The output is cut into 256 x 256 tiles, one per workgroup, which the device runs
+ * in rounds of one tile per compute unit.  When the last round is at most half full, each of its
+ * tiles is split along K into 2..8 parts: the parts run as separate workgroups that write their
+ * unscaled fp32 sums to the workspace, and a second kernel adds a tile's parts in part order,
+ * applies s_dA * s_dB and stores C.  The result is deterministic, within the same bound of the
+ * exact sum as nvfp4_gemm's, but its last bits can differ from nvfp4_gemm's for the split tiles
+ * (another fp32 addition order).  workspace: device, 16-byte aligned, ws_bytes of it usable;
+ * with NULL or fewer bytes than nvfp4_gemm_workspace_size this call is exactly nvfp4_gemm.  Its
+ * contents on return are unspecified; calls that may overlap in time need distinct workspaces.
+ * Shapes, layouts and errors as nvfp4_gemm; a misaligned workspace: NVFP4_ERR_ALIGN. */
+NVFP4_API nvfp4_status nvfp4_gemm_ws(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
+                                     int64_t ldc, void *workspace, size_t ws_bytes, void *stream);
 
 /* Format sweep [P2 Describir: block size, scale format and rounding method are the FP4 design
  * choices explored, and 16-element blocks with E4M3 scales (NVFP4) come out best]: quantize

@@ -24,7 +24,8 @@ SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_qu
            "nvfp4_quantize_2d", "nvfp4_hadamard_quantize", "nvfp4_dequantize", "nvfp4_gemm",
            "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual",
            "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t", "nvfp4_amax_accumulate",
-           "nvfp4_hadamard_amax_accumulate", "nvfp4_hadamard_quantize_noise")
+           "nvfp4_hadamard_amax_accumulate", "nvfp4_hadamard_quantize_noise", "nvfp4_gemm_ws",
+           "nvfp4_gemm_workspace_size")
 
 
 class NvTensor(C.Structure):
@@ -58,6 +59,8 @@ def lib():
         L.nvfp4_hadamard_quantize_noise.argtypes = [P, i32, i64, u64, P, i32, u64, T, P, P]
         L.nvfp4_dequantize.argtypes = [T, P, i32, i64, P]
         L.nvfp4_gemm.argtypes = [T, T, P, i32, i64, P]
+        L.nvfp4_gemm_ws.argtypes = [T, T, P, i32, i64, P, C.c_size_t, P]
+        L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, C.POINTER(C.c_size_t)]
         L.mxfp4_quantize_1d.argtypes = [P, i32, i64, i32, u64, T, P]
         L.mxfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.mxfp4_quantize_1d_t.argtypes = [P, i32, i64, i32, u64, T, P]
@@ -299,13 +302,33 @@ def dequantize(q: QTensor, dtype: torch.dtype = torch.float32, out: torch.Tensor
     return y
 
 
+def gemm_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace with which ``nvfp4_gemm_ws`` splits an M x N x K GEMM (0: no split)."""
+    n = C.c_size_t(0)
+    _check("nvfp4_gemm_workspace_size", lib().nvfp4_gemm_workspace_size(M, N, K, C.byref(n)))
+    return int(n.value)
+
+
 def gemm(a: QTensor, b: QTensor, dtype: torch.dtype = torch.float32,
-         out: torch.Tensor | None = None) -> torch.Tensor:
-    """C = A * B^T (A [M x K], B [N x K]) with fp32 accumulation."""
+         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         split: bool = True) -> torch.Tensor:
+    """C = A * B^T (A [M x K], B [N x K]) with fp32 accumulation.  With ``split`` (the default)
+    the call is ``nvfp4_gemm_ws``: a partly empty last round of output tiles is split along K into
+    the workspace (``workspace``, a uint8 device tensor, or one allocated here when it is needed);
+    ``split=False`` calls ``nvfp4_gemm``."""
     c = torch.empty((a.rows, b.rows), dtype=dtype, device=a.codes.device) if out is None else out
     da, db = a.desc(), b.desc()
-    _check("nvfp4_gemm", lib().nvfp4_gemm(C.byref(da), C.byref(db), _ptr(c), _dtype_code(c.dtype),
-                                          c.stride(0), _stream(c.device)))
+    if not split:
+        _check("nvfp4_gemm", lib().nvfp4_gemm(C.byref(da), C.byref(db), _ptr(c),
+                                              _dtype_code(c.dtype), c.stride(0), _stream(c.device)))
+        return c
+    need = gemm_workspace_size(a.rows, b.rows, a.cols)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=c.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("nvfp4_gemm_ws", lib().nvfp4_gemm_ws(C.byref(da), C.byref(db), _ptr(c),
+                                                _dtype_code(c.dtype), c.stride(0), _ptr(workspace),
+                                                nbytes, _stream(c.device)))
     return c
 
 

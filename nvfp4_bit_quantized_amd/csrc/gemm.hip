@@ -86,16 +86,17 @@ __device__ __forceinline__ int chunk_swz(int r, int q) { return q ^ (r & 7) ^ ((
 
 struct FastAddrU {
     const uint8_t *pa, *pb, *psa, *psb;
+    // Addresses of step kb (the first step of this workgroup's K range).
     __device__ __forceinline__ void init(const OperandDesc& A, const OperandDesc& B, int64_t m0,
-                                         int64_t n0, int K, int t) {
+                                         int64_t n0, int K, int t, int kb) {
         const int r = t >> 1, h = t & 1;
         int64_t ra = m0 + r, rb = n0 + r;
         ra = ra < A.rows - 1 ? ra : A.rows - 1;
         rb = rb < B.rows - 1 ? rb : B.rows - 1;
-        pa = A.codes + ra * (K / 2) + h * 16;
-        pb = B.codes + rb * (K / 2) + h * 16;
-        psa = A.scales + (A.tiled ? ra / 16 : ra) * (K / 16) + h * 2;
-        psb = B.scales + (B.tiled ? rb / 16 : rb) * (K / 16) + h * 2;
+        pa = A.codes + ra * (K / 2) + (int64_t)kb * kRowBytes + h * 16;
+        pb = B.codes + rb * (K / 2) + (int64_t)kb * kRowBytes + h * 16;
+        psa = A.scales + (A.tiled ? ra / 16 : ra) * (K / 16) + kb * 4 + h * 2;
+        psb = B.scales + (B.tiled ? rb / 16 : rb) * (K / 16) + kb * 4 + h * 2;
     }
     // Fetch step kt, then advance to step kt + 1 unless kt is the last step: fetches past the
     // end re-read the last step (the caller never stores them), so no load is conditional.
@@ -117,10 +118,10 @@ struct FastAddrU {
 struct GuardedAddrU {
     OperandDesc A, B;
     int64_t m0, n0;
-    int K, t;
+    int K, t, kstep0;
     __device__ __forceinline__ void init(const OperandDesc& a, const OperandDesc& b, int64_t m,
-                                         int64_t n, int k, int tid) {
-        A = a; B = b; m0 = m; n0 = n; K = k; t = tid;
+                                         int64_t n, int k, int tid, int kb) {
+        A = a; B = b; m0 = m; n0 = n; K = k; t = tid; kstep0 = kb;
     }
     __device__ __forceinline__ uint4 chunk(const OperandDesc& op, int64_t row, int k0) const {
         const int kk = k0 + (t & 1) * 32;
@@ -143,7 +144,7 @@ struct GuardedAddrU {
     // Steps past K read as zeros.
     __device__ __forceinline__ FetchU fetch(int kt, int) {
         FetchU f;
-        const int k0 = kt * kBK;
+        const int k0 = (kt + kstep0) * kBK;
         const int64_t ra = m0 + (t >> 1), rb = n0 + (t >> 1);
         f.a = chunk(A, ra, k0);
         f.b = chunk(B, rb, k0);
@@ -251,11 +252,45 @@ __device__ __forceinline__ void step_pipe(const LdsStepU& cur, LdsStepU& nxt, co
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// One wave's accumulators, unscaled, into a dense fp32 256 x 256 partial tile P (row stride 256),
+// at the wave's offset (r0, c0) inside the tile.  Both accumulator layouts (see mfma_frags).
+template <int TM, int TN, bool kT>
+__device__ __forceinline__ void store_partial(const float16v (&acc)[TM][TN], int lane, int r0,
+                                              int c0, float* __restrict__ P) {
+    const int lrow = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (kT) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int row = r0 + i * 32 + lrow, col = c0 + j * 32 + 8 * g + 4 * h;
+                    *reinterpret_cast<float4*>(P + row * kTile + col) =
+                        make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                    acc[i][j][4 * g + 3]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    P[row * kTile + j * 32 + c0 + lrow] = acc[i][j][r];
+                }
+            }
+        }
+}
+
 // Waves are arranged WM x WN over the 256 x 256 tile, each owning TM x TN MFMA tiles of 32x32.
+// Workgroups [0, full) each compute one whole output tile.  When the tile count leaves the last
+// round of the device partly empty, the remaining tiles are split along K: workgroup full + u
+// computes split u % splits (K steps [j nk / splits, (j + 1) nk / splits)) of tile full + u /
+// splits and stores its unscaled fp32 sums into the partial tile ws + u * 256 * 256, which
+// k_splitk_fixup then adds in split order.
 template <int WM, int WN, int TM, int TN, bool kBF16Out, typename Addr>
 __global__ void __launch_bounds__(kThreads)
 k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __restrict__ sdA,
-             const float* __restrict__ sdB, void* __restrict__ C, int64_t ldc) {
+             const float* __restrict__ sdB, void* __restrict__ C, int64_t ldc, uint32_t full,
+             uint32_t splits, float* __restrict__ ws) {
     static_assert(WM * WN == kThreads / 64 && WM * TM * 32 == kTile && WN * TN * 32 == kTile, "tile");
     static_assert(sizeof(LdsStepU) * 2 >= (kThreads / 64) * 16384, "epilogue staging");
     constexpr bool kT = kBF16Out;          // accumulator layout suited to each epilogue
@@ -263,8 +298,18 @@ k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __r
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const uint32_t nbm = (M + kTile - 1) / kTile, nbn = (N + kTile - 1) / kTile;
+    const int nk_all = (K + kBK - 1) / kBK;
+    uint32_t tile = blockIdx.x;
+    int kb = 0, nk = nk_all;
+    const bool split = blockIdx.x >= full;           // uniform over the workgroup
+    if (split) {
+        const uint32_t u = blockIdx.x - full, j = u % splits;
+        tile = full + u / splits;
+        kb = (int)(((int64_t)j * nk_all) / splits);
+        nk = (int)(((int64_t)(j + 1) * nk_all) / splits) - kb;
+    }
     uint32_t bm, bn;
-    tile_coords(blockIdx.x, nbm, nbn, bm, bn);
+    tile_coords(tile, nbm, nbn, bm, bn);
     const int64_t m0 = (int64_t)bm * kTile, n0 = (int64_t)bn * kTile;
 
     float16v acc[TM][TN];
@@ -276,8 +321,7 @@ k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __r
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     Addr addr;
-    addr.init(A, B, m0, n0, K, tid);
-    const int nk = (K + kBK - 1) / kBK;
+    addr.init(A, B, m0, n0, K, tid, kb);
     FetchU fa = addr.fetch(0, nk);
     store_step_u(st[0], fa, tid);
     FetchU fb = addr.fetch(1, nk);
@@ -307,6 +351,11 @@ k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __r
     if (kt < nk) step_pipe<TM, TN, kT>(st[0], st[1], fb, false, acc, f0, f1, wm, wn, lane, tid);
     mfma_frags<TM, TN, kT>(f1, acc);                   // sub-step 3 of the last step
 
+    if (split) {
+        store_partial<TM, TN, kT>(acc, lane, wm * TM * 32, wn * TN * 32,
+                                  ws + (size_t)(blockIdx.x - full) * (kTile * kTile));
+        return;
+    }
     const float alpha = (*sdA) * (*sdB);
     const int64_t r0 = m0 + wm * TM * 32, c0 = n0 + wn * TN * 32;
     if constexpr (kBF16Out) {
@@ -321,30 +370,109 @@ k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __r
     }
 }
 
+// The tiles split along K: C = alpha * (P_0 + P_1 + ... + P_{splits-1}), the partials added in
+// split order (so the result does not depend on which workgroup finished first), alpha = s_dA *
+// s_dB.  One workgroup of 256 threads per 8 rows of a tile, 8 consecutive columns per thread.
+template <bool kBF16Out>
+__global__ void __launch_bounds__(256)
+k_splitk_fixup(const float* __restrict__ ws, uint32_t full, uint32_t splits, int M, int N,
+               const float* __restrict__ sdA, const float* __restrict__ sdB, void* __restrict__ C,
+               int64_t ldc) {
+    constexpr int kRowsPerBlock = 8;
+    const uint32_t t_local = blockIdx.x / (kTile / kRowsPerBlock);
+    const int row = (blockIdx.x % (kTile / kRowsPerBlock)) * kRowsPerBlock + (threadIdx.x >> 5);
+    const int col = (threadIdx.x & 31) * 8;
+    const uint32_t nbm = (M + kTile - 1) / kTile, nbn = (N + kTile - 1) / kTile;
+    uint32_t bm, bn;
+    tile_coords(full + t_local, nbm, nbn, bm, bn);
+    const float* p = ws + (size_t)t_local * splits * (kTile * kTile) + row * kTile + col;
+    float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
+    for (uint32_t j = 1; j < splits; ++j) {
+        const float4 a = *reinterpret_cast<const float4*>(p + (size_t)j * (kTile * kTile));
+        const float4 b = *reinterpret_cast<const float4*>(p + (size_t)j * (kTile * kTile) + 4);
+        lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+        hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+    }
+    const float alpha = (*sdA) * (*sdB);
+    const float v[8] = {lo.x * alpha, lo.y * alpha, lo.z * alpha, lo.w * alpha,
+                        hi.x * alpha, hi.y * alpha, hi.z * alpha, hi.w * alpha};
+    const int64_t gr = (int64_t)bm * kTile + row, gc = (int64_t)bn * kTile + col;
+    if (gr >= M) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (gc + e >= N) break;
+        if constexpr (kBF16Out)
+            reinterpret_cast<uint16_t*>(C)[gr * ldc + gc + e] = (uint16_t)f32_to_bf16(v[e]);
+        else
+            reinterpret_cast<float*>(C)[gr * ldc + gc + e] = v[e];
+    }
+}
+
+// Split plan: the whole tiles of full rounds of the device's compute units run unsplit; when
+// the last round is at most half full its tiles are split along K into `splits` parts (at most
+// 8, each at least kMinSplitSteps K steps), so that the round's units fill the device.
+struct SplitPlan {
+    uint32_t full, tail, splits;
+    size_t ws_bytes;
+};
+
+constexpr int kMinSplitSteps = 16;
+constexpr uint32_t kMaxSplits = 8;
+
+inline SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int cus) {
+    const uint32_t tiles = (uint32_t)(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile));
+    SplitPlan p{tiles, 0, 1, 0};
+    if (cus <= 0 || K % kBK != 0) return p;
+    const uint32_t tail = tiles % (uint32_t)cus;
+    if (tail == 0) return p;
+    uint32_t s = (uint32_t)cus / tail;
+    s = s < kMaxSplits ? s : kMaxSplits;
+    const int64_t nk = K / kBK;
+    while (s > 1 && nk / s < kMinSplitSteps) --s;
+    if (s < 2) return p;
+    p.full = tiles - tail;
+    p.tail = tail;
+    p.splits = s;
+    p.ws_bytes = (size_t)tail * s * kTile * kTile * sizeof(float);
+    return p;
+}
+
+inline int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
 template <int WM, int WN, int TM, int TN>
 static void launch_gemm(const OperandDesc& a, const OperandDesc& b, int M, int N, int K,
                         const float* sdA, const float* sdB, void* c, bool bf16, int64_t ldc,
-                        hipStream_t st) {
-    const uint32_t nbm = (M + kTile - 1) / kTile, nbn = (N + kTile - 1) / kTile;
-    const dim3 grid(nbm * nbn), block(kThreads);
+                        const SplitPlan& plan, float* ws, hipStream_t st) {
+    const dim3 grid(plan.full + plan.tail * plan.splits), block(kThreads);
     const bool fast = K % kBK == 0;
 #define NVFP4_GEMM_LAUNCH(BF, ADDR)                                                               \
     hipLaunchKernelGGL((k_gemm_nvfp4<WM, WN, TM, TN, BF, ADDR>), grid, block, 0, st, a, b, M, N, \
-                       K, sdA, sdB, c, ldc)
+                       K, sdA, sdB, c, ldc, plan.full, plan.splits, ws)
     if (bf16) {
         if (fast) NVFP4_GEMM_LAUNCH(true, FastAddrU); else NVFP4_GEMM_LAUNCH(true, GuardedAddrU);
     } else {
         if (fast) NVFP4_GEMM_LAUNCH(false, FastAddrU); else NVFP4_GEMM_LAUNCH(false, GuardedAddrU);
     }
 #undef NVFP4_GEMM_LAUNCH
+    if (plan.tail) {
+        const dim3 fgrid(plan.tail * (kTile / 8));
+        if (bf16)
+            hipLaunchKernelGGL(k_splitk_fixup<true>, fgrid, dim3(256), 0, st, ws, plan.full,
+                               plan.splits, M, N, sdA, sdB, c, ldc);
+        else
+            hipLaunchKernelGGL(k_splitk_fixup<false>, fgrid, dim3(256), 0, st, ws, plan.full,
+                               plan.splits, M, N, sdA, sdB, c, ldc);
+    }
 }
 
-}  // namespace nvfp4
-
-using namespace nvfp4;
-
-extern "C" nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
-                                   nvfp4_dtype c_dt, int64_t ldc, void* stream) {
+// Argument checks shared by the GEMM entry points; on success fills the operand descriptors.
+static nvfp4_status check_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, const void* c,
+                               nvfp4_dtype c_dt, int64_t ldc) {
     nvfp4_status s = check_q(a, NVFP4_BLK_1x16, false);
     if (s) return s;
     if (!b) return NVFP4_ERR_NULL;
@@ -358,14 +486,55 @@ extern "C" nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     const int64_t M = a->rows, N = b->rows, K = a->cols;
     if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return NVFP4_ERR_SHAPE;
     if (((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile) >= (1ll << 31)) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+// plan: the split plan to run (a plan with tail == 0 runs every tile whole); ws: its partials.
+static nvfp4_status run_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                             nvfp4_dtype c_dt, int64_t ldc, const SplitPlan& plan, float* ws,
+                             hipStream_t st) {
+    const int64_t M = a->rows, N = b->rows, K = a->cols;
     if (M == 0 || N == 0) return NVFP4_OK;
     if (K == 0) {                                  // no codes to read (they may be null)
-        launch_zero_c(c, c_dt == NVFP4_BF16, ldc, (int)M, (int)N, as_stream(stream));
+        launch_zero_c(c, c_dt == NVFP4_BF16, ldc, (int)M, (int)N, st);
         return launch_status();
     }
     const OperandDesc da{a->codes, a->scales, M, 0};
     const OperandDesc db{b->codes, b->scales, N, b->layout == NVFP4_BLK_16x16 ? 1 : 0};
     launch_gemm<2, 4, 4, 2>(da, db, (int)M, (int)N, (int)K, a->s_dec, b->s_dec, c,
-                            c_dt == NVFP4_BF16, ldc, as_stream(stream));
+                            c_dt == NVFP4_BF16, ldc, plan, ws, st);
     return launch_status();
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" nvfp4_status nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                                   nvfp4_dtype c_dt, int64_t ldc, void* stream) {
+    const nvfp4_status s = check_gemm(a, b, c, c_dt, ldc);
+    if (s) return s;
+    const SplitPlan whole{(uint32_t)(((a->rows + kTile - 1) / kTile) * ((b->rows + kTile - 1) / kTile)),
+                          0, 1, 0};
+    return run_gemm(a, b, c, c_dt, ldc, whole, nullptr, as_stream(stream));
+}
+
+extern "C" nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+    if (!bytes) return NVFP4_ERR_NULL;
+    if (M < 0 || N < 0 || K < 0 || M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31))
+        return NVFP4_ERR_SHAPE;
+    *bytes = (M == 0 || N == 0 || K == 0) ? 0 : plan_split(M, N, K, device_cus()).ws_bytes;
+    return NVFP4_OK;
+}
+
+extern "C" nvfp4_status nvfp4_gemm_ws(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                                      nvfp4_dtype c_dt, int64_t ldc, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+    const nvfp4_status s = check_gemm(a, b, c, c_dt, ldc);
+    if (s) return s;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    SplitPlan plan = plan_split(a->rows, b->rows, a->cols, device_cus());
+    if (plan.tail && (!workspace || ws_bytes < plan.ws_bytes))
+        plan = SplitPlan{plan.full + plan.tail, 0, 1, 0};        // too small: whole tiles only
+    return run_gemm(a, b, c, c_dt, ldc, plan, static_cast<float*>(workspace), as_stream(stream));
 }
