@@ -62,7 +62,8 @@ typedef enum {
     NVFP4_ERR_DTYPE = 3,    /* unknown dtype or rounding mode */
     NVFP4_ERR_ALIGN = 4,    /* a pointer or row stride is not 16-byte aligned */
     NVFP4_ERR_LAYOUT = 5,   /* a tensor's block layout is not allowed for this call */
-    NVFP4_ERR_LAUNCH = 6    /* the HIP runtime rejected a kernel launch */
+    NVFP4_ERR_LAUNCH = 6,   /* the HIP runtime rejected a kernel launch */
+    NVFP4_ERR_SCRATCH = 7   /* the call needs more than the library's fixed scratch buffer */
 } nvfp4_status;
 
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
@@ -242,6 +243,18 @@ NVFP4_API nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K
  * Shapes, layouts and errors as nvfp4_gemm; a misaligned workspace: NVFP4_ERR_ALIGN. */
 NVFP4_API nvfp4_status nvfp4_gemm_ws(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                                      int64_t ldc, void *workspace, size_t ws_bytes, void *stream);
+
+/* nvfp4_gemm_ws for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid allocation): the split partial tiles go to a scratch
+ * array that the library holds in device memory, 64 MiB per device (256 partial tiles of 256 x
+ * 256 fp32), from the first call on a device until the process ends.  Same result as nvfp4_gemm_ws
+ * with a large enough workspace, bit for bit.  A shape whose split needs more than 64 MiB (only
+ * possible on a device with more than 256 compute units) returns NVFP4_ERR_SCRATCH and enqueues
+ * nothing; a failed lookup of the array's device address returns NVFP4_ERR_LAUNCH.  Every call
+ * on one device shares that device's array: calls that overlap in time on one device (other
+ * streams, other host threads) race and must be ordered by the caller.  Allocates nothing. */
+NVFP4_API nvfp4_status nvfp4_gemm_ws_noalloc(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c,
+                                             nvfp4_dtype c_dt, int64_t ldc, void *stream);
 
 /* Format sweep [P2 Describir: block size, scale format and rounding method are the FP4 design
  * choices explored, and 16-element blocks with E4M3 scales (NVFP4) come out best]: quantize

@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_LAYOUT, ERR_LAUNCH = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_LAYOUT, ERR_LAUNCH, ERR_SCRATCH = range(8)
 F32, BF16 = 0, 1
 RNE, SR = 0, 1
 BLK_1x16, BLK_16x16, MX_1x32 = 0, 1, 2
@@ -25,7 +25,7 @@ SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_qu
            "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual",
            "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t", "nvfp4_amax_accumulate",
            "nvfp4_hadamard_amax_accumulate", "nvfp4_hadamard_quantize_noise", "nvfp4_gemm_ws",
-           "nvfp4_gemm_workspace_size")
+           "nvfp4_gemm_workspace_size", "nvfp4_gemm_ws_noalloc")
 
 
 class NvTensor(C.Structure):
@@ -61,6 +61,7 @@ def lib():
         L.nvfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.nvfp4_gemm_ws.argtypes = [T, T, P, i32, i64, P, C.c_size_t, P]
         L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, C.POINTER(C.c_size_t)]
+        L.nvfp4_gemm_ws_noalloc.argtypes = [T, T, P, i32, i64, P]
         L.mxfp4_quantize_1d.argtypes = [P, i32, i64, i32, u64, T, P]
         L.mxfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.mxfp4_quantize_1d_t.argtypes = [P, i32, i64, i32, u64, T, P]

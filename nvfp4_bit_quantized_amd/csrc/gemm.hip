@@ -34,6 +34,8 @@
 #include "gemm_common.hpp"
 #include "host_util.hpp"
 
+#include <atomic>
+
 
 namespace nvfp4 {
 
@@ -506,6 +508,27 @@ static nvfp4_status run_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void*
     return launch_status();
 }
 
+// Scratch of the allocation-free entry point: the split partial tiles, at most 256 of 256 x 256
+// fp32 (64 MiB), in one array per device that lives as long as the process.  Host code uses
+// only the device address that hipGetSymbolAddress returns for the current device, looked up
+// on the first call on that device and kept per device.
+constexpr size_t kScratchBytes = (size_t)256 * kTile * kTile * sizeof(float);
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+static float* scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return static_cast<float*>(p);
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -537,4 +560,15 @@ extern "C" nvfp4_status nvfp4_gemm_ws(const nvfp4_tensor* a, const nvfp4_tensor*
     if (plan.tail && (!workspace || ws_bytes < plan.ws_bytes))
         plan = SplitPlan{plan.full + plan.tail, 0, 1, 0};        // too small: whole tiles only
     return run_gemm(a, b, c, c_dt, ldc, plan, static_cast<float*>(workspace), as_stream(stream));
+}
+
+extern "C" nvfp4_status nvfp4_gemm_ws_noalloc(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                                              nvfp4_dtype c_dt, int64_t ldc, void* stream) {
+    const nvfp4_status s = check_gemm(a, b, c, c_dt, ldc);
+    if (s) return s;
+    const SplitPlan plan = plan_split(a->rows, b->rows, a->cols, device_cus());
+    if (plan.ws_bytes > kScratchBytes) return NVFP4_ERR_SCRATCH;
+    float* ws = nullptr;
+    if (plan.tail && !(ws = scratch_ptr())) return NVFP4_ERR_LAUNCH;
+    return run_gemm(a, b, c, c_dt, ldc, plan, ws, as_stream(stream));
 }

@@ -553,6 +553,7 @@ extern "C" const char* nvfp4_status_string(nvfp4_status s) {
         case NVFP4_ERR_ALIGN: return "pointer or row stride not 16-byte aligned";
         case NVFP4_ERR_LAYOUT: return "tensor layout not allowed for this call";
         case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+        case NVFP4_ERR_SCRATCH: return "the call needs more than the library's fixed scratch buffer";
     }
     return "unknown status";
 }

@@ -49,7 +49,7 @@ def test_exports_nothing_else(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(99) == b"unknown status"
 
