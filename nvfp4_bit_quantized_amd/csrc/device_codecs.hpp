@@ -46,21 +46,18 @@ __device__ __forceinline__ void publish_amax(float* dst, float m) {
 }
 
 // ---- E4M3 (OCP E4M3FN), non-negative operands -----------------------------------------------
-// Round to nearest even with saturation at 448 (0x7E); values below 2^-6 use the subnormal
-// quantum 2^-9.  Branch-free: both candidate encodings are formed and one is selected.
+// Round to nearest even with saturation at 448 (0x7E), subnormals (quantum 2^-9) included.
+// gfx950's v_cvt_pk_fp8_f32 rounds fp32 to OCP E4M3 to nearest even with E4M3 subnormals; the
+// clamp to 448 first supplies the saturation (it would give NaN above 464).  Checked bit for bit
+// against a software encoder (the nearest of the 127 values, ties to even) for every fp32 bit
+// pattern in [0, 448] and, clamped, up to 2^20.
 __device__ __forceinline__ uint32_t e4m3_encode(float t) {
-    const uint32_t sub = (uint32_t)__builtin_rintf(t * 512.0f);     // t < 2^-6: multiples of 2^-9
-    uint32_t b = __float_as_uint(t);
-    b += 0x7FFFFu + ((b >> 20) & 1u);                               // mantissa to 3 bits, RNE
-    uint32_t nrm = (b >> 20) - 960u;                                // exponent bias 127 -> 7
-    nrm = nrm < 0x7Eu ? nrm : 0x7Eu;
-    return t < 0x1p-6f ? sub : (t >= 448.0f ? 0x7Eu : nrm);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
+// v_cvt_f32_fp8: exact for every E4M3 byte (all 127 non-negative finite bytes checked).
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
-    const float sub = (float)(b & 7u) * 0x1p-9f;
-    const float nrm = __uint_as_float((b + 960u) << 20);
-    return b < 8u ? sub : nrm;
+    return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
 }
 
 // Block step: scale byte and the element encode factor s_enc / scale (0 for a zero scale).
@@ -72,6 +69,32 @@ __device__ __forceinline__ void block_scale(float amax_b, const TensorScales& ts
     const float d = scale_byte == 0 ? 1.0f : e4m3_decode(scale_byte);
     const float e = ts.s_enc / d;
     enc = scale_byte == 0 ? 0.0f : e;
+}
+
+// The encode factors of one tensor for every scale byte, enc[b] = fl(s_enc / dec(b)) (0 for
+// b = 0; byte 0x7F is never produced), filled once per workgroup so that a block looks up its
+// factor instead of dividing: the same single correctly rounded division, done 127 times per
+// workgroup instead of once per block.
+struct EncTable {
+    float v[128];
+};
+
+// Every thread of the workgroup must call this (it ends with a barrier).
+__device__ __forceinline__ void fill_enc_table(EncTable& t, const TensorScales& ts) {
+    for (uint32_t b = threadIdx.x; b < 128; b += blockDim.x) {
+        const bool zero = b == 0 || b == 127;
+        const float e = ts.s_enc / (zero ? 1.0f : e4m3_decode(b));
+        t.v[b] = zero ? 0.0f : e;
+    }
+    __syncthreads();
+}
+
+// block_scale with the factor from the workgroup's table (bit-identical).
+__device__ __forceinline__ void block_scale_tab(float amax_b, const TensorScales& ts,
+                                                const EncTable& t, uint32_t& scale_byte,
+                                                float& enc) {
+    scale_byte = e4m3_encode(amax_b * ts.k1);
+    enc = t.v[scale_byte];
 }
 
 // ---- E2M1 [P1 Caracteristicas: 1 sign, 2 exponent, 1 mantissa bit] --------------------------

@@ -283,7 +283,8 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
 template <typename T, bool kSR, bool kNoise>
 __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, const RhtCoords& rc,
                                                       int64_t Tn, int64_t F, uint32_t mask,
-                                                      const TensorScales& ts, uint64_t seed,
+                                                      const TensorScales& ts, const EncTable& tab,
+                                                      uint64_t seed,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales, double& g2,
                                                       double& e2) {
@@ -305,7 +306,7 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
         for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
         uint32_t sb;
         float enc;
-        block_scale(m, ts, sb, enc);
+        block_scale_tab(m, ts, tab, sb, enc);
         float z[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) z[e] = v[e] * enc;
@@ -337,7 +338,8 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
 // are valid or neither is.
 template <typename T, bool kSR>
 __device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const RhtCoords& rc,
-                                                int64_t F, const TensorScales& ts, uint64_t seed,
+                                                int64_t F, const TensorScales& ts,
+                                                const EncTable& tab, uint64_t seed,
                                                 uint8_t* __restrict__ codes,
                                                 uint8_t* __restrict__ scales) {
     const bool lead = (threadIdx.x & 1) == 0;
@@ -357,7 +359,7 @@ __device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const R
         m = fmaxf(m, swap_adjacent(m));
         uint32_t sb;
         float enc;
-        block_scale(m, ts, sb, enc);
+        block_scale_tab(m, ts, tab, sb, enc);
         float z[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = y[e] * enc;
@@ -389,6 +391,8 @@ k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t
         *amax_out = A;
         *sdec_out = ts.s_dec;
     }
+    __shared__ EncTable tab;
+    fill_enc_table(tab, ts);
     const uint32_t mask = rht_sign_mask(sign_seed);
     double g2 = 0.0, e2 = 0.0;
     if constexpr (kNoise) {
@@ -400,8 +404,8 @@ k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t
             if (rc.valid) {
                 Tile16x8<T> tile;
                 tile.load(x + rc.c * 16 * ld + rc.f0, ld);
-                quant_tile_transposed<T, kSR, true>(tile, rc, Tn, F, mask, ts, seed, codes, scales,
-                                                    g2, e2);
+                quant_tile_transposed<T, kSR, true>(tile, rc, Tn, F, mask, ts, tab, seed, codes,
+                                                    scales, g2, e2);
             }
         }
         publish_noise<kRhtThreads>(g2, e2, ts, sums);
@@ -410,8 +414,8 @@ k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t
         if (!rc.valid) return;
         Tile16x8<T> tile;
         tile.load(x + rc.c * 16 * ld + rc.f0, ld);
-        quant_tile_transposed<T, kSR, false>(tile, rc, Tn, F, mask, ts, seed, codes, scales, g2,
-                                             e2);
+        quant_tile_transposed<T, kSR, false>(tile, rc, Tn, F, mask, ts, tab, seed, codes, scales,
+                                             g2, e2);
     }
 }
 
@@ -434,15 +438,18 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
         *amax_t_out = At;
         *sdec_t_out = tst.s_dec;
     }
+    __shared__ EncTable tab, tab_t;
+    fill_enc_table(tab, ts);
+    fill_enc_table(tab_t, tst);
     const RhtCoords rc = rht_coords(Tn, F);
     if (!rc.valid) return;
     const uint32_t mask = rht_sign_mask(sign_seed);
     Tile16x8<T> tile;
     tile.load(x + rc.c * 16 * ld + rc.f0, ld);
-    quant_tile_rows<T, kSR>(tile, rc, F, ts, seed, codes, scales);
+    quant_tile_rows<T, kSR>(tile, rc, F, ts, tab, seed, codes, scales);
     double g2 = 0.0, e2 = 0.0;             // unused: the dual quantizer has no noise sums
-    quant_tile_transposed<T, kSR, false>(tile, rc, Tn, F, mask, tst, seed_t, codes_t, scales_t, g2,
-                                         e2);
+    quant_tile_transposed<T, kSR, false>(tile, rc, Tn, F, mask, tst, tab_t, seed_t, codes_t,
+                                         scales_t, g2, e2);
 }
 
 // MXFP4 quantization of x^T [P3 NVFP4 in pratica: MXFP4, 32-element blocks with power-of-two

@@ -123,7 +123,8 @@ static int amax_grid(uint32_t groups) {
 template <typename T, bool kSR, bool kNoise>
 __device__ __forceinline__ void quant1d_blocks(const T* __restrict__ x, int64_t ld, uint32_t blocks,
                                                FastDiv bpr, uint32_t cols, const TensorScales& ts,
-                                               uint64_t seed, uint2* __restrict__ codes,
+                                               const EncTable& tab, uint64_t seed,
+                                               uint2* __restrict__ codes,
                                                uint8_t* __restrict__ scales, uint32_t base,
                                                double& g2, double& e2) {
     float y[kQUnroll][16];
@@ -146,7 +147,7 @@ __device__ __forceinline__ void quant1d_blocks(const T* __restrict__ x, int64_t 
         for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(y[u][e]));
         uint32_t sb;
         float enc;
-        block_scale(m, ts, sb, enc);
+        block_scale_tab(m, ts, tab, sb, enc);
         float z[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) z[e] = y[u][e] * enc;
@@ -180,6 +181,8 @@ k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uin
         *amax_out = A;
         *sdec_out = ts.s_dec;
     }
+    __shared__ EncTable tab;
+    fill_enc_table(tab, ts);
     // With kNoise the grid is capped and each workgroup strides over the blocks, so that few
     // workgroups publish sums (same-address fp64 atomics serialize); otherwise the grid covers
     // every block once.
@@ -187,10 +190,10 @@ k_quant1d(const T* __restrict__ x, int64_t ld, uint32_t blocks, FastDiv bpr, uin
     if constexpr (kNoise) {
         for (uint32_t wbase = blockIdx.x * kThreads * kQUnroll; wbase < blocks;
              wbase += gridDim.x * kThreads * kQUnroll)
-            quant1d_blocks<T, kSR, kNoise>(x, ld, blocks, bpr, cols, ts, seed, codes, scales,
+            quant1d_blocks<T, kSR, kNoise>(x, ld, blocks, bpr, cols, ts, tab, seed, codes, scales,
                                            wbase + threadIdx.x, g2, e2);
     } else {
-        quant1d_blocks<T, kSR, kNoise>(x, ld, blocks, bpr, cols, ts, seed, codes, scales,
+        quant1d_blocks<T, kSR, kNoise>(x, ld, blocks, bpr, cols, ts, tab, seed, codes, scales,
                                        blockIdx.x * kThreads * kQUnroll + threadIdx.x, g2, e2);
     }
     if constexpr (kNoise) publish_noise<kThreads>(g2, e2, ts, sums);
