@@ -176,6 +176,20 @@ __device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
     return rht_coords_at(T, F, blockIdx.x, blockIdx.y);
 }
 
+// XCD-aware placement for a 1D grid of n = gx * gy tiles (gx feature blocks per 512-token row of
+// tiles).  Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2, so
+// workgroup w runs on XCD w % 8; tile t = (w % 8) * (n / 8) + w / 8 gives every XCD a contiguous
+// range of tiles, i.e. runs of adjacent feature blocks of the same tokens.  The row-wise code and
+// scale bytes of one token row, written a few bytes per workgroup, then meet in one L2 and
+// leave as whole lines instead of as partial lines from eight L2s.  n % 8 != 0: t = w.
+__device__ __forceinline__ RhtCoords rht_coords_xcd(int64_t T, int64_t F) {
+    const uint32_t w = blockIdx.x, n = gridDim.x;
+    const uint32_t gx = (uint32_t)((F + kFeatPerBlock - 1) / kFeatPerBlock);
+    const uint32_t t = (n & 7u) == 0 ? (w & 7u) * (n >> 3) + (w >> 3) : w;
+    const uint32_t by = t / gx;
+    return rht_coords_at(T, F, t - by * gx, by);
+}
+
 // Persistent over (64-feature x 512-token) tiles, at most kRhtAmaxBlocks workgroups, each
 // publishing its maximum once (publish_amax).  The factor 1/4 of the transform is applied to the
 // maximum instead of to every element: scaling by 1/4 and fp32 rounding are both monotonic, so
@@ -441,7 +455,7 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
     __shared__ EncTable tab, tab_t;
     fill_enc_table(tab, ts);
     fill_enc_table(tab_t, tst);
-    const RhtCoords rc = rht_coords(Tn, F);
+    const RhtCoords rc = rht_coords_xcd(Tn, F);
     if (!rc.valid) return;
     const uint32_t mask = rht_sign_mask(sign_seed);
     Tile16x8<T> tile;
@@ -696,7 +710,9 @@ extern "C" nvfp4_status nvfp4_quantize_dual(const void* x, nvfp4_dtype dt, int64
         hipLaunchKernelGGL(k_scalars_rht, dim3(1), dim3(1), 0, st, src_t, out_t->amax, out_t->s_dec);
         return launch_status();
     }
-    const dim3 grid = rht_grid(T, F), block(kRhtThreads);
+    const dim3 g2 = rht_grid(T, F), block(kRhtThreads);
+    if ((int64_t)g2.x * g2.y >= (1ll << 31)) return NVFP4_ERR_SHAPE;
+    const dim3 grid(g2.x * g2.y);              // tiles placed by rht_coords_xcd
 #define NVFP4_DQ(TT, SRV)                                                                         \
     hipLaunchKernelGGL((k_dual_quant<TT, SRV>), grid, block, 0, st, static_cast<const TT*>(x), T, \
                        F, ld, sign_seed, src, src_t, seed, seed_t, out->codes, out->scales,        \
