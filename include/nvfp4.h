@@ -299,6 +299,19 @@ NVFP4_API nvfp4_status mxfp4_quantize_1d_t(const void *x, nvfp4_dtype dt, int64_
 NVFP4_API nvfp4_status mxfp4_gemm(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
                                   int64_t ldc, void *stream);
 
+/* Bytes of workspace with which mxfp4_gemm_ws splits an M x N x K GEMM on the current device (0:
+ * no split; only K % 256 == 0 GEMMs split, in parts of at least 4 steps of 256).  At most
+ * 64 MiB.  Errors as nvfp4_gemm_workspace_size. */
+NVFP4_API nvfp4_status mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, size_t *bytes);
+
+/* mxfp4_gemm with a caller-owned device workspace, splitting a partly empty last round of output
+ * tiles along K exactly as nvfp4_gemm_ws does [P3 NVFP4 in pratica: the comparison format gets
+ * the same GEMM schedule]: deterministic, bit-for-bit different from mxfp4_gemm only in the fp32
+ * addition order of the split tiles; with NULL or too small a workspace exactly mxfp4_gemm.
+ * Workspace rules as nvfp4_gemm_ws. */
+NVFP4_API nvfp4_status mxfp4_gemm_ws(const nvfp4_tensor *a, const nvfp4_tensor *b, void *c, nvfp4_dtype c_dt,
+                                     int64_t ldc, void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,8 @@ SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_qu
            "mxfp4_quantize_1d", "mxfp4_gemm", "nvfp4_dual_amax", "nvfp4_quantize_dual",
            "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t", "nvfp4_amax_accumulate",
            "nvfp4_hadamard_amax_accumulate", "nvfp4_hadamard_quantize_noise", "nvfp4_gemm_ws",
-           "nvfp4_gemm_workspace_size", "nvfp4_gemm_ws_noalloc")
+           "nvfp4_gemm_workspace_size", "nvfp4_gemm_ws_noalloc", "mxfp4_gemm_ws",
+           "mxfp4_gemm_workspace_size")
 
 
 class NvTensor(C.Structure):
@@ -62,6 +63,8 @@ def lib():
         L.nvfp4_gemm_ws.argtypes = [T, T, P, i32, i64, P, C.c_size_t, P]
         L.nvfp4_gemm_workspace_size.argtypes = [i64, i64, i64, C.POINTER(C.c_size_t)]
         L.nvfp4_gemm_ws_noalloc.argtypes = [T, T, P, i32, i64, P]
+        L.mxfp4_gemm_ws.argtypes = [T, T, P, i32, i64, P, C.c_size_t, P]
+        L.mxfp4_gemm_workspace_size.argtypes = [i64, i64, i64, C.POINTER(C.c_size_t)]
         L.mxfp4_quantize_1d.argtypes = [P, i32, i64, i32, u64, T, P]
         L.mxfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.mxfp4_quantize_1d_t.argtypes = [P, i32, i64, i32, u64, T, P]
@@ -354,10 +357,28 @@ def mx_quantize_1d_t(x: torch.Tensor, rounding: int = RNE, seed: int = 0,
     return q
 
 
+def mx_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace with which ``mxfp4_gemm_ws`` splits an M x N x K GEMM (0: no split)."""
+    n = C.c_size_t(0)
+    _check("mxfp4_gemm_workspace_size", lib().mxfp4_gemm_workspace_size(M, N, K, C.byref(n)))
+    return int(n.value)
+
+
 def mx_gemm(a: QTensor, b: QTensor, dtype: torch.dtype = torch.float32,
-            out: torch.Tensor | None = None) -> torch.Tensor:
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+            split: bool = True) -> torch.Tensor:
+    """C = A * B^T for MXFP4 operands; ``split`` and ``workspace`` as for ``gemm``."""
     c = torch.empty((a.rows, b.rows), dtype=dtype, device=a.codes.device) if out is None else out
     da, db = a.desc(), b.desc()
-    _check("mxfp4_gemm", lib().mxfp4_gemm(C.byref(da), C.byref(db), _ptr(c), _dtype_code(c.dtype),
-                                          c.stride(0), _stream(c.device)))
+    if not split:
+        _check("mxfp4_gemm", lib().mxfp4_gemm(C.byref(da), C.byref(db), _ptr(c),
+                                              _dtype_code(c.dtype), c.stride(0), _stream(c.device)))
+        return c
+    need = mx_gemm_workspace_size(a.rows, b.rows, a.cols)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=c.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mxfp4_gemm_ws", lib().mxfp4_gemm_ws(C.byref(da), C.byref(db), _ptr(c),
+                                                _dtype_code(c.dtype), c.stride(0), _ptr(workspace),
+                                                nbytes, _stream(c.device)))
     return c

@@ -39,6 +39,8 @@
 
 namespace nvfp4 {
 
+constexpr int kMinSplitSteps = 16;   // K steps of 64 per split part, at least
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
@@ -254,34 +256,6 @@ __device__ __forceinline__ void step_pipe(const LdsStepU& cur, LdsStepU& nxt, co
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// One wave's accumulators, unscaled, into a dense fp32 256 x 256 partial tile P (row stride 256),
-// at the wave's offset (r0, c0) inside the tile.  Both accumulator layouts (see mfma_frags).
-template <int TM, int TN, bool kT>
-__device__ __forceinline__ void store_partial(const float16v (&acc)[TM][TN], int lane, int r0,
-                                              int c0, float* __restrict__ P) {
-    const int lrow = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (kT) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int row = r0 + i * 32 + lrow, col = c0 + j * 32 + 8 * g + 4 * h;
-                    *reinterpret_cast<float4*>(P + row * kTile + col) =
-                        make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                    acc[i][j][4 * g + 3]);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = r0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    P[row * kTile + j * 32 + c0 + lrow] = acc[i][j][r];
-                }
-            }
-        }
-}
-
 // Waves are arranged WM x WN over the 256 x 256 tile, each owning TM x TN MFMA tiles of 32x32.
 // Workgroups [0, full) each compute one whole output tile.  When the tile count leaves the last
 // round of the device partly empty, the remaining tiles are split along K: workgroup full + u
@@ -372,80 +346,6 @@ k_gemm_nvfp4(OperandDesc A, OperandDesc B, int M, int N, int K, const float* __r
     }
 }
 
-// The tiles split along K: C = alpha * (P_0 + P_1 + ... + P_{splits-1}), the partials added in
-// split order (so the result does not depend on which workgroup finished first), alpha = s_dA *
-// s_dB.  One workgroup of 256 threads per 8 rows of a tile, 8 consecutive columns per thread.
-template <bool kBF16Out>
-__global__ void __launch_bounds__(256)
-k_splitk_fixup(const float* __restrict__ ws, uint32_t full, uint32_t splits, int M, int N,
-               const float* __restrict__ sdA, const float* __restrict__ sdB, void* __restrict__ C,
-               int64_t ldc) {
-    constexpr int kRowsPerBlock = 8;
-    const uint32_t t_local = blockIdx.x / (kTile / kRowsPerBlock);
-    const int row = (blockIdx.x % (kTile / kRowsPerBlock)) * kRowsPerBlock + (threadIdx.x >> 5);
-    const int col = (threadIdx.x & 31) * 8;
-    const uint32_t nbm = (M + kTile - 1) / kTile, nbn = (N + kTile - 1) / kTile;
-    uint32_t bm, bn;
-    tile_coords(full + t_local, nbm, nbn, bm, bn);
-    const float* p = ws + (size_t)t_local * splits * (kTile * kTile) + row * kTile + col;
-    float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
-    for (uint32_t j = 1; j < splits; ++j) {
-        const float4 a = *reinterpret_cast<const float4*>(p + (size_t)j * (kTile * kTile));
-        const float4 b = *reinterpret_cast<const float4*>(p + (size_t)j * (kTile * kTile) + 4);
-        lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
-        hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
-    }
-    const float alpha = (*sdA) * (*sdB);
-    const float v[8] = {lo.x * alpha, lo.y * alpha, lo.z * alpha, lo.w * alpha,
-                        hi.x * alpha, hi.y * alpha, hi.z * alpha, hi.w * alpha};
-    const int64_t gr = (int64_t)bm * kTile + row, gc = (int64_t)bn * kTile + col;
-    if (gr >= M) return;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        if (gc + e >= N) break;
-        if constexpr (kBF16Out)
-            reinterpret_cast<uint16_t*>(C)[gr * ldc + gc + e] = (uint16_t)f32_to_bf16(v[e]);
-        else
-            reinterpret_cast<float*>(C)[gr * ldc + gc + e] = v[e];
-    }
-}
-
-// Split plan: the whole tiles of full rounds of the device's compute units run unsplit; when
-// the last round is at most half full its tiles are split along K into `splits` parts (at most
-// 8, each at least kMinSplitSteps K steps), so that the round's units fill the device.
-struct SplitPlan {
-    uint32_t full, tail, splits;
-    size_t ws_bytes;
-};
-
-constexpr int kMinSplitSteps = 16;
-constexpr uint32_t kMaxSplits = 8;
-
-inline SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int cus) {
-    const uint32_t tiles = (uint32_t)(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile));
-    SplitPlan p{tiles, 0, 1, 0};
-    if (cus <= 0 || K % kBK != 0) return p;
-    const uint32_t tail = tiles % (uint32_t)cus;
-    if (tail == 0) return p;
-    uint32_t s = (uint32_t)cus / tail;
-    s = s < kMaxSplits ? s : kMaxSplits;
-    const int64_t nk = K / kBK;
-    while (s > 1 && nk / s < kMinSplitSteps) --s;
-    if (s < 2) return p;
-    p.full = tiles - tail;
-    p.tail = tail;
-    p.splits = s;
-    p.ws_bytes = (size_t)tail * s * kTile * kTile * sizeof(float);
-    return p;
-}
-
-inline int device_cus() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    return n;
-}
-
 template <int WM, int WN, int TM, int TN>
 static void launch_gemm(const OperandDesc& a, const OperandDesc& b, int M, int N, int K,
                         const float* sdA, const float* sdB, void* c, bool bf16, int64_t ldc,
@@ -461,15 +361,7 @@ static void launch_gemm(const OperandDesc& a, const OperandDesc& b, int M, int N
         if (fast) NVFP4_GEMM_LAUNCH(false, FastAddrU); else NVFP4_GEMM_LAUNCH(false, GuardedAddrU);
     }
 #undef NVFP4_GEMM_LAUNCH
-    if (plan.tail) {
-        const dim3 fgrid(plan.tail * (kTile / 8));
-        if (bf16)
-            hipLaunchKernelGGL(k_splitk_fixup<true>, fgrid, dim3(256), 0, st, ws, plan.full,
-                               plan.splits, M, N, sdA, sdB, c, ldc);
-        else
-            hipLaunchKernelGGL(k_splitk_fixup<false>, fgrid, dim3(256), 0, st, ws, plan.full,
-                               plan.splits, M, N, sdA, sdB, c, ldc);
-    }
+    launch_splitk_fixup(plan, ws, M, N, sdA, sdB, c, bf16, ldc, st);
 }
 
 // Argument checks shared by the GEMM entry points; on success fills the operand descriptors.
@@ -546,7 +438,7 @@ extern "C" nvfp4_status nvfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t 
     if (!bytes) return NVFP4_ERR_NULL;
     if (M < 0 || N < 0 || K < 0 || M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31))
         return NVFP4_ERR_SHAPE;
-    *bytes = (M == 0 || N == 0 || K == 0) ? 0 : plan_split(M, N, K, device_cus()).ws_bytes;
+    *bytes = (M == 0 || N == 0 || K == 0) ? 0 : plan_split(M, N, K, device_cus(), kBK, kMinSplitSteps).ws_bytes;
     return NVFP4_OK;
 }
 
@@ -556,7 +448,7 @@ extern "C" nvfp4_status nvfp4_gemm_ws(const nvfp4_tensor* a, const nvfp4_tensor*
     const nvfp4_status s = check_gemm(a, b, c, c_dt, ldc);
     if (s) return s;
     if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
-    SplitPlan plan = plan_split(a->rows, b->rows, a->cols, device_cus());
+    SplitPlan plan = plan_split(a->rows, b->rows, a->cols, device_cus(), kBK, kMinSplitSteps);
     if (plan.tail && (!workspace || ws_bytes < plan.ws_bytes))
         plan = SplitPlan{plan.full + plan.tail, 0, 1, 0};        // too small: whole tiles only
     return run_gemm(a, b, c, c_dt, ldc, plan, static_cast<float*>(workspace), as_stream(stream));
@@ -566,7 +458,7 @@ extern "C" nvfp4_status nvfp4_gemm_ws_noalloc(const nvfp4_tensor* a, const nvfp4
                                               nvfp4_dtype c_dt, int64_t ldc, void* stream) {
     const nvfp4_status s = check_gemm(a, b, c, c_dt, ldc);
     if (s) return s;
-    const SplitPlan plan = plan_split(a->rows, b->rows, a->cols, device_cus());
+    const SplitPlan plan = plan_split(a->rows, b->rows, a->cols, device_cus(), kBK, kMinSplitSteps);
     if (plan.ws_bytes > kScratchBytes) return NVFP4_ERR_SCRATCH;
     float* ws = nullptr;
     if (plan.tail && !(ws = scratch_ptr())) return NVFP4_ERR_LAUNCH;

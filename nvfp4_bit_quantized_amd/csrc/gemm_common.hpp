@@ -4,6 +4,7 @@
 #pragma once
 
 #include "device_codecs.hpp"
+#include "host_util.hpp"
 
 namespace nvfp4 {
 
@@ -97,6 +98,126 @@ __device__ __forceinline__ void epilogue_f32(const float16v (&acc)[TM][TN], floa
                 if (row < M) C[row * ldc + col] = acc[i][j][r] * alpha;
             }
         }
+}
+
+// ---- split last round ------------------------------------------------------------------------
+constexpr int kGemmTile = 256;      // output tile of both GEMM kernels (BM = BN)
+
+// One wave's accumulators, unscaled, into a dense fp32 256 x 256 partial tile P (row stride 256),
+// at the wave's offset (r0, c0) inside the tile.  Both accumulator layouts (see mfma_frags).
+template <int TM, int TN, bool kT>
+__device__ __forceinline__ void store_partial(const float16v (&acc)[TM][TN], int lane, int r0,
+                                              int c0, float* __restrict__ P) {
+    const int lrow = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (kT) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int row = r0 + i * 32 + lrow, col = c0 + j * 32 + 8 * g + 4 * h;
+                    *reinterpret_cast<float4*>(P + row * kGemmTile + col) =
+                        make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                    acc[i][j][4 * g + 3]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    P[row * kGemmTile + j * 32 + c0 + lrow] = acc[i][j][r];
+                }
+            }
+        }
+}
+
+// The tiles split along K: C = alpha * (P_0 + P_1 + ... + P_{splits-1}), the partials added in
+// split order (so the result does not depend on which workgroup finished first), alpha = s_dA *
+// s_dB (1 when sdA is null: MXFP4 has no tensor scales).  One workgroup of 256 threads per 8 rows
+// of a tile, 8 consecutive columns per thread.
+template <bool kBF16Out>
+__global__ void __launch_bounds__(256)
+k_splitk_fixup(const float* __restrict__ ws, uint32_t full, uint32_t splits, int M, int N,
+               const float* __restrict__ sdA, const float* __restrict__ sdB, void* __restrict__ C,
+               int64_t ldc) {
+    constexpr int kRowsPerBlock = 8;
+    const uint32_t t_local = blockIdx.x / (kGemmTile / kRowsPerBlock);
+    const int row = (blockIdx.x % (kGemmTile / kRowsPerBlock)) * kRowsPerBlock + (threadIdx.x >> 5);
+    const int col = (threadIdx.x & 31) * 8;
+    const uint32_t nbm = (M + kGemmTile - 1) / kGemmTile, nbn = (N + kGemmTile - 1) / kGemmTile;
+    uint32_t bm, bn;
+    tile_coords(full + t_local, nbm, nbn, bm, bn);
+    const float* p = ws + (size_t)t_local * splits * (kGemmTile * kGemmTile) + row * kGemmTile + col;
+    float4 lo = *reinterpret_cast<const float4*>(p), hi = *reinterpret_cast<const float4*>(p + 4);
+    for (uint32_t j = 1; j < splits; ++j) {
+        const float4 a = *reinterpret_cast<const float4*>(p + (size_t)j * (kGemmTile * kGemmTile));
+        const float4 b = *reinterpret_cast<const float4*>(p + (size_t)j * (kGemmTile * kGemmTile) + 4);
+        lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+        hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+    }
+    const float alpha = sdA ? (*sdA) * (*sdB) : 1.0f;
+    const float v[8] = {lo.x * alpha, lo.y * alpha, lo.z * alpha, lo.w * alpha,
+                        hi.x * alpha, hi.y * alpha, hi.z * alpha, hi.w * alpha};
+    const int64_t gr = (int64_t)bm * kGemmTile + row, gc = (int64_t)bn * kGemmTile + col;
+    if (gr >= M) return;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (gc + e >= N) break;
+        if constexpr (kBF16Out)
+            reinterpret_cast<uint16_t*>(C)[gr * ldc + gc + e] = (uint16_t)f32_to_bf16(v[e]);
+        else
+            reinterpret_cast<float*>(C)[gr * ldc + gc + e] = v[e];
+    }
+}
+
+// Split plan: the whole tiles of full rounds of the device's compute units run unsplit; when
+// the last round is at most half full its tiles are split along K into `splits` parts (at most
+// 8, each at least min_steps K steps of `step` elements), so that the round's units fill the
+// device.
+struct SplitPlan {
+    uint32_t full, tail, splits;
+    size_t ws_bytes;
+};
+
+constexpr uint32_t kMaxSplits = 8;
+
+inline SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int cus, int step, int min_steps) {
+    const uint32_t tiles = (uint32_t)(((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile));
+    SplitPlan p{tiles, 0, 1, 0};
+    if (cus <= 0 || K % step != 0) return p;
+    const uint32_t tail = tiles % (uint32_t)cus;
+    if (tail == 0) return p;
+    uint32_t s = (uint32_t)cus / tail;
+    s = s < kMaxSplits ? s : kMaxSplits;
+    const int64_t nk = K / step;
+    while (s > 1 && nk / s < min_steps) --s;
+    if (s < 2) return p;
+    p.full = tiles - tail;
+    p.tail = tail;
+    p.splits = s;
+    p.ws_bytes = (size_t)tail * s * kGemmTile * kGemmTile * sizeof(float);
+    return p;
+}
+
+inline int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
+// The fixup of a split plan's last round (nothing when the plan has no split tiles).
+inline void launch_splitk_fixup(const SplitPlan& plan, const float* ws, int M, int N,
+                                const float* sdA, const float* sdB, void* c, bool bf16,
+                                int64_t ldc, hipStream_t st) {
+    if (!plan.tail) return;
+    const dim3 grid(plan.tail * (kGemmTile / 8)), block(256);
+    if (bf16)
+        hipLaunchKernelGGL(k_splitk_fixup<true>, grid, block, 0, st, ws, plan.full, plan.splits, M,
+                           N, sdA, sdB, c, ldc);
+    else
+        hipLaunchKernelGGL(k_splitk_fixup<false>, grid, block, 0, st, ws, plan.full, plan.splits, M,
+                           N, sdA, sdB, c, ldc);
 }
 
 // C = 0 when the inner dimension is empty (K == 0: every dot product is an empty sum).  Grid-

@@ -258,16 +258,17 @@ __device__ __forceinline__ int d2_swz(int r, int c) { return c ^ ((r >> 1) & 7);
 struct MxDma2 {
     const uint8_t *a[4], *b[4], *s0, *s1;
     int nk;
+    // Sources of steps [kb, kb + nsteps) (the workgroup's K range).
     __device__ __forceinline__ void init(const MxOperand& A, const MxOperand& B, int64_t m0,
-                                         int64_t n0, int K, int wave, int lane) {
+                                         int64_t n0, int K, int wave, int lane, int kb, int nsteps) {
         const int64_t rb = K / 2, nkb = K / 32;
         const int64_t ma = A.rows - 1, mb = B.rows - 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int rr = (4 * wave + j) * 8 + (lane >> 3);
             const int c = d2_swz(rr, lane & 7);
-            a[j] = A.codes + (m0 + rr < ma ? m0 + rr : ma) * rb + c * 16;
-            b[j] = B.codes + (n0 + rr < mb ? n0 + rr : mb) * rb + c * 16;
+            a[j] = A.codes + (m0 + rr < ma ? m0 + rr : ma) * rb + (int64_t)kb * kD2RowBytes + c * 16;
+            b[j] = B.codes + (n0 + rr < mb ? n0 + rr : mb) * rb + (int64_t)kb * kD2RowBytes + c * 16;
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -275,10 +276,11 @@ struct MxDma2 {
             const bool isb = v >= 8;
             const int half = (v >> 2) & 1;
             const int64_t r = (isb ? n0 : m0) + (v & 3) * 64 + lane, last = isb ? mb : ma;
-            const uint8_t* p = (isb ? B.scales : A.scales) + (r < last ? r : last) * nkb + half * 4;
+            const uint8_t* p = (isb ? B.scales : A.scales) + (r < last ? r : last) * nkb +
+                               (int64_t)kb * 8 + half * 4;
             if (u == 0) s0 = p; else s1 = p;
         }
-        nk = K / kD2BK;
+        nk = nsteps;
     }
     __device__ __forceinline__ void issue(int step, uint32_t stage, int wave) const {
         const int64_t k = step < nk ? step : nk - 1;
@@ -320,9 +322,13 @@ __device__ __forceinline__ void d2_read_frags(const MxStage2& st, MxFrags<TM, TN
     }
 }
 
+// Workgroups [0, full) compute whole tiles; with a split plan, workgroup full + u computes part
+// u % splits (steps [j nk / splits, (j + 1) nk / splits)) of tile full + u / splits into the
+// fp32 partial tile ws + u * 256 * 256, which k_splitk_fixup adds in part order.
 template <int WM, int WN, int TM, int TN, bool kBF16Out>
 __global__ void __launch_bounds__(kMxThreads)
-k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict__ C, int64_t ldc) {
+k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict__ C, int64_t ldc,
+                uint32_t full, uint32_t splits, float* __restrict__ ws) {
     constexpr bool kT = kBF16Out;
     constexpr int kRing = 2 * (int)sizeof(MxStage2), kStaging = (kMxThreads / 64) * 16384;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kRing > kStaging ? kRing : kStaging];
@@ -332,8 +338,18 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const uint32_t nbm = (M + kMxTile - 1) / kMxTile, nbn = (N + kMxTile - 1) / kMxTile;
+    const int nk_all = K / kD2BK;
+    uint32_t tile = blockIdx.x;
+    int kb = 0, nsteps = nk_all;
+    const bool split = blockIdx.x >= full;           // uniform over the workgroup
+    if (split) {
+        const uint32_t u = blockIdx.x - full, j = u % splits;
+        tile = full + u / splits;
+        kb = (int)(((int64_t)j * nk_all) / splits);
+        nsteps = (int)(((int64_t)(j + 1) * nk_all) / splits) - kb;
+    }
     uint32_t bm, bn;
-    tile_coords(blockIdx.x, nbm, nbn, bm, bn);
+    tile_coords(tile, nbm, nbn, bm, bn);
     const int64_t m0 = (int64_t)bm * kMxTile, n0 = (int64_t)bn * kMxTile;
 
     float16v acc[TM][TN];
@@ -345,7 +361,7 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     MxDma2 dma;
-    dma.init(A, B, m0, n0, K, wave, lane);
+    dma.init(A, B, m0, n0, K, wave, lane, kb, nsteps);
     const int nk = dma.nk;
     dma.issue(0, lds0, wave);
     MxFrags<TM, TN> f0, f1;
@@ -382,6 +398,11 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
     mx_mfma<TM, TN, kT, 3>(f1, acc);                    // sub-step 3 of the last step
     wait_vmcnt<0>();                                    // the clamped re-fetches past the end
 
+    if (split) {
+        store_partial<TM, TN, kT>(acc, lane, wm * TM * 32, wn * TN * 32,
+                                  ws + (size_t)(blockIdx.x - full) * (kMxTile * kMxTile));
+        return;
+    }
     const int64_t r0 = m0 + wm * TM * 32, c0 = n0 + wn * TN * 32;
     if constexpr (kBF16Out) {
         const bool vec = (reinterpret_cast<uintptr_t>(C) & 15u) == 0 && (ldc * 2) % 16 == 0;
@@ -542,12 +563,10 @@ k_gemm_mxfp4_any(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict_
     }
 }
 
-}  // namespace nvfp4
+constexpr int kMxMinSplitSteps = 4;    // K steps of 256 per split part, at least
 
-using namespace nvfp4;
-
-extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
-                                   nvfp4_dtype c_dt, int64_t ldc, void* stream) {
+static nvfp4_status check_mx_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, const void* c,
+                                  nvfp4_dtype c_dt, int64_t ldc) {
     nvfp4_status s = check_q(a, MXFP4_BLK_1x32, false);
     if (s) return s;
     s = check_q(b, MXFP4_BLK_1x32, false);
@@ -559,8 +578,23 @@ extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     if (M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31)) return NVFP4_ERR_SHAPE;
     if (((M + kMxTile - 1) / kMxTile) * ((N + kMxTile - 1) / kMxTile) >= (1ll << 31))
         return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+// The plan of a K % 256 == 0 GEMM (the only kernel that splits); whole tiles otherwise.
+static SplitPlan mx_plan(int64_t M, int64_t N, int64_t K) {
+    if (K % kD2BK != 0) {
+        const uint32_t tiles = (uint32_t)(((M + kMxTile - 1) / kMxTile) * ((N + kMxTile - 1) / kMxTile));
+        return SplitPlan{tiles, 0, 1, 0};
+    }
+    return plan_split(M, N, K, device_cus(), kD2BK, kMxMinSplitSteps);
+}
+
+static nvfp4_status run_mx_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                                nvfp4_dtype c_dt, int64_t ldc, const SplitPlan& plan, float* ws,
+                                hipStream_t st) {
+    const int64_t M = a->rows, N = b->rows, K = a->cols;
     if (M == 0 || N == 0) return NVFP4_OK;
-    hipStream_t st = as_stream(stream);
     const bool bf16 = c_dt == NVFP4_BF16;
     if (K == 0) {                                  // no codes to read (they may be null)
         launch_zero_c(c, bf16, ldc, (int)M, (int)N, st);
@@ -570,12 +604,14 @@ extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
     const dim3 grid(nbm * nbn);
     if (K % kD2BK == 0) {
         const MxOperand da{a->codes, a->scales, M}, db{b->codes, b->scales, N};
+        const dim3 g2(plan.full + plan.tail * plan.splits);
         if (bf16)
-            hipLaunchKernelGGL((k_gemm_mxfp4_d2<2, 4, 4, 2, true>), grid, dim3(kMxThreads), 0, st,
-                               da, db, (int)M, (int)N, (int)K, c, ldc);
+            hipLaunchKernelGGL((k_gemm_mxfp4_d2<2, 4, 4, 2, true>), g2, dim3(kMxThreads), 0, st,
+                               da, db, (int)M, (int)N, (int)K, c, ldc, plan.full, plan.splits, ws);
         else
-            hipLaunchKernelGGL((k_gemm_mxfp4_d2<2, 4, 4, 2, false>), grid, dim3(kMxThreads), 0, st,
-                               da, db, (int)M, (int)N, (int)K, c, ldc);
+            hipLaunchKernelGGL((k_gemm_mxfp4_d2<2, 4, 4, 2, false>), g2, dim3(kMxThreads), 0, st,
+                               da, db, (int)M, (int)N, (int)K, c, ldc, plan.full, plan.splits, ws);
+        launch_splitk_fixup(plan, ws, (int)M, (int)N, nullptr, nullptr, c, bf16, ldc, st);
     } else if (K % kMxBK == 0) {
         const MxOperand da{a->codes, a->scales, M}, db{b->codes, b->scales, N};
         if (bf16)
@@ -593,4 +629,36 @@ extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b,
                                a->codes, a->scales, b->codes, b->scales, (int)M, (int)N, (int)K, c, ldc);
     }
     return launch_status();
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" nvfp4_status mxfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                                   nvfp4_dtype c_dt, int64_t ldc, void* stream) {
+    const nvfp4_status s = check_mx_gemm(a, b, c, c_dt, ldc);
+    if (s) return s;
+    const uint32_t tiles = (uint32_t)(((a->rows + kMxTile - 1) / kMxTile) * ((b->rows + kMxTile - 1) / kMxTile));
+    return run_mx_gemm(a, b, c, c_dt, ldc, SplitPlan{tiles, 0, 1, 0}, nullptr, as_stream(stream));
+}
+
+extern "C" nvfp4_status mxfp4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+    if (!bytes) return NVFP4_ERR_NULL;
+    if (M < 0 || N < 0 || K < 0 || M >= (1ll << 31) || N >= (1ll << 31) || K >= (1ll << 31))
+        return NVFP4_ERR_SHAPE;
+    *bytes = (M == 0 || N == 0 || K == 0) ? 0 : mx_plan(M, N, K).ws_bytes;
+    return NVFP4_OK;
+}
+
+extern "C" nvfp4_status mxfp4_gemm_ws(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                                      nvfp4_dtype c_dt, int64_t ldc, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+    const nvfp4_status s = check_mx_gemm(a, b, c, c_dt, ldc);
+    if (s) return s;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    SplitPlan plan = mx_plan(a->rows, b->rows, a->cols);
+    if (plan.tail && (!workspace || ws_bytes < plan.ws_bytes))
+        plan = SplitPlan{plan.full + plan.tail, 0, 1, 0};        // too small: whole tiles only
+    return run_mx_gemm(a, b, c, c_dt, ldc, plan, static_cast<float*>(workspace), as_stream(stream));
 }

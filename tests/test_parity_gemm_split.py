@@ -130,3 +130,34 @@ def test_split_gemm_wgrad_shape(nv, orc):
     ref = orc.gemm_f64(_oq(qdyt), _oq(qxt), FF, D, T, rows=rows)
     got = c[torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
     assert_gemm_close(got, ref, "wgrad 20480x5120x16384 split")
+
+
+def test_mx_split_gemm_matches_oracle(nv, orc):
+    """mxfp4_gemm_ws: 12 tiles of a K % 256 == 0 GEMM split 8 ways (ragged edges), against the
+    float64 MXFP4 oracle; deterministic; bf16 = RNE of fp32; too small a workspace = mxfp4_gemm."""
+    import ctypes as C
+    M, N, K = 1000, 520, 8192
+    need = nv.mx_gemm_workspace_size(M, N, K)
+    assert need > 0
+    qa = nv.mx_quantize_1d(W.act((M, K), 91).to(DEV))
+    qb = nv.mx_quantize_1d(W.act((N, K), 92).to(DEV))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    c = nv.mx_gemm(qa, qb, torch.float32, workspace=ws)
+    assert _ran_split(ws)
+    oa = dict(codes=qa.codes.cpu().numpy(), scales=qa.scales.cpu().numpy())
+    ob = dict(codes=qb.codes.cpu().numpy(), scales=qb.scales.cpu().numpy())
+    ref = orc.mx_gemm_f64(oa, ob, M, N, K)
+    assert_gemm_close(c.cpu().numpy(), ref, "mx split 1000x520x8192")
+    c2 = nv.mx_gemm(qa, qb, torch.float32, workspace=ws)
+    cb = nv.mx_gemm(qa, qb, torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(c, c2)
+    assert torch.equal(cb.view(torch.int16), c.to(torch.bfloat16).view(torch.int16))
+    whole = nv.mx_gemm(qa, qb, torch.float32, split=False)
+    out = torch.full_like(whole, float("nan"))
+    da, db = qa.desc(), qb.desc()
+    rc = nv.lib().mxfp4_gemm_ws(C.byref(da), C.byref(db), out.data_ptr(), nv.F32, out.stride(0),
+                                ws.data_ptr(), need - 1, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == nv.OK and torch.equal(out, whole)
+    assert nv.mx_gemm_workspace_size(M, N, K + 128) == 0          # K % 256 != 0: no split
