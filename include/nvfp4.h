@@ -36,7 +36,7 @@
  *     < 2^31, i.e. fewer than 2^34 elements (NVFP4_ERR_SHAPE beyond).  The token-major calls
  *     (Hadamard, dual, transposing MXFP4) take T <= 33553920 tokens (ceil(T / 512) <= 65535
  *     workgroup rows) and F < 2^31 features; nvfp4_quantize_dual also needs its workgroup count
- *     ceil(F / 64) * ceil(T / 512) below 2^31.
+ *     ceil(F / 256) * ceil(T / 256) below 2^31.
  */
 #ifndef NVFP4_H
 #define NVFP4_H

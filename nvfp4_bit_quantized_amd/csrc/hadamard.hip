@@ -176,20 +176,6 @@ __device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
     return rht_coords_at(T, F, blockIdx.x, blockIdx.y);
 }
 
-// XCD-aware placement for a 1D grid of n = gx * gy tiles (gx feature blocks per 512-token row of
-// tiles).  Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2, so
-// workgroup w runs on XCD w % 8; tile t = (w % 8) * (n / 8) + w / 8 gives every XCD a contiguous
-// range of tiles, i.e. runs of adjacent feature blocks of the same tokens.  The row-wise code and
-// scale bytes of one token row, written a few bytes per workgroup, then meet in one L2 and
-// leave as whole lines instead of as partial lines from eight L2s.  n % 8 != 0: t = w.
-__device__ __forceinline__ RhtCoords rht_coords_xcd(int64_t T, int64_t F) {
-    const uint32_t w = blockIdx.x, n = gridDim.x;
-    const uint32_t gx = (uint32_t)((F + kFeatPerBlock - 1) / kFeatPerBlock);
-    const uint32_t t = (n & 7u) == 0 ? (w & 7u) * (n >> 3) + (w >> 3) : w;
-    const uint32_t by = t / gx;
-    return rht_coords_at(T, F, t - by * gx, by);
-}
-
 // Persistent over (64-feature x 512-token) tiles, at most kRhtAmaxBlocks workgroups, each
 // publishing its maximum once (publish_amax).  The factor 1/4 of the transform is applied to the
 // maximum instead of to every element: scaling by 1/4 and fp32 rounding are both monotonic, so
@@ -292,21 +278,16 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
     }
 }
 
-// The transposed copy of one thread's tile: for each of its 8 features, the 16 tokens of its
-// chunk through (1/4) H16 D, one NVFP4 block of row `feature` of the [F x T] output.
-template <typename T, bool kSR, bool kNoise>
-__device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, const RhtCoords& rc,
-                                                      int64_t Tn, int64_t F, uint32_t mask,
+// The transposed copy of one thread's tile (features f0 .. f0 + 7 of the 16 tokens from row0):
+// for each feature f, the 16 tokens through (1/4) H16 D, one NVFP4 block of row f0 + f of the
+// [F x T] output, handed to emit(f, lo, hi, scale_byte) (codes of tokens 0-7 in lo, 8-15 in hi).
+template <typename T, bool kSR, bool kNoise, typename Emit>
+__device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, int64_t f0,
+                                                      int64_t row0, int64_t Tn, uint32_t mask,
                                                       const TensorScales& ts, const EncTable& tab,
-                                                      uint64_t seed,
-                                                      uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales, double& g2,
-                                                      double& e2) {
-    // Offsets of feature f0's output row; each further feature adds one row (64-bit additions
-    // instead of a 64-bit multiply per feature).
-    uint64_t idx = (uint64_t)rc.f0 * (uint64_t)Tn + (uint64_t)rc.c * 16;    // SR element index
-    uint8_t* cp = codes + rc.f0 * (Tn / 2) + rc.c * 8;
-    uint8_t* sp = scales + rc.f0 * (Tn / 16) + rc.c;
+                                                      uint64_t seed, double& g2, double& e2,
+                                                      Emit emit) {
+    uint64_t idx = (uint64_t)f0 * (uint64_t)Tn + (uint64_t)row0;    // SR element index
     Tile16x8<T> sgn = tile;
     sgn.apply_signs(__builtin_amdgcn_readfirstlane(mask));     // the same in every lane
 #pragma unroll
@@ -334,34 +315,23 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, c
             lo = e2m1_rne_pack8(z);
             hi = e2m1_rne_pack8(z + 8);
         }
-        if (rc.f0 + f < F) {
-            *reinterpret_cast<uint2*>(cp) = make_uint2(lo, hi);
-            *sp = (uint8_t)sb;
-            if constexpr (kNoise) block_noise(v, lo, hi, sb, ts, g2, e2);
-        }
+        emit(f, lo, hi, sb);
+        if constexpr (kNoise) block_noise(v, lo, hi, sb, ts, g2, e2);
         idx += (uint64_t)Tn;
-        cp += Tn / 2;
-        sp += Tn / 16;
     }
 }
 
-// The row-wise copy of one thread's tile: for each of its 16 token rows, its 8 features are one
-// half of a 16-feature NVFP4 block whose other half sits in the adjacent lane (lane ^ 1, which
-// holds the same rows and the next or previous 8 features); the block amax is shared with one
-// DPP lane swap and the even lane writes the scale byte.  F % 16 == 0, so both lanes of a pair
-// are valid or neither is.
-template <typename T, bool kSR>
-__device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const RhtCoords& rc,
+// The row-wise copy of one thread's tile (features f0 .. f0 + 7 of token rows row0 .. row0 + 15):
+// for each row i, its 8 features are one half of a 16-feature NVFP4 block whose other half sits
+// in the adjacent lane (lane ^ 1, which holds the same rows and the next or previous 8
+// features); the block amax is shared with one DPP lane swap, and emit(i, codes, scale_byte)
+// receives the 8 codes (both lanes of a pair get the block's scale byte).  F % 16 == 0, so both
+// lanes of a pair are valid or neither is.
+template <typename T, bool kSR, typename Emit>
+__device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, int64_t f0, int64_t row0,
                                                 int64_t F, const TensorScales& ts,
-                                                const EncTable& tab, uint64_t seed,
-                                                uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales) {
-    const bool lead = (threadIdx.x & 1) == 0;
-    // Offsets of the chunk's first token row; each further row adds F elements.
-    const int64_t row0 = rc.c * 16;
-    uint64_t idx = (uint64_t)row0 * (uint64_t)F + (uint64_t)rc.f0;          // SR element index
-    uint8_t* cp = codes + row0 * (F / 2) + rc.f0 / 2;
-    uint8_t* sp = scales + row0 * (F / 16) + rc.f0 / 16;
+                                                const EncTable& tab, uint64_t seed, Emit emit) {
+    uint64_t idx = (uint64_t)row0 * (uint64_t)F + (uint64_t)f0;          // SR element index
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         float y[8];
@@ -385,15 +355,27 @@ __device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, const R
         } else {
             packed = e2m1_rne_pack8(z);
         }
-        *reinterpret_cast<uint32_t*>(cp) = packed;
-        if (lead) *sp = (uint8_t)sb;
+        emit(i, packed, sb);
         idx += (uint64_t)F;
-        cp += F / 2;
-        sp += F / 16;
     }
 }
 
-template <typename T, bool kSR, bool kNoise>
+// Stores of the transposed copy straight to the [F x T] output: feature f0 + f's row, 8 code
+// bytes and one scale byte for the thread's chunk.
+struct GlobalColumnSink {
+    uint8_t* cp;          // codes of feature f0, chunk c
+    uint8_t* sp;          // scale byte of feature f0, chunk c
+    int64_t code_row, scale_row;
+    __device__ __forceinline__ void operator()(int f, uint32_t lo, uint32_t hi, uint32_t sb) const {
+        *reinterpret_cast<uint2*>(cp + f * code_row) = make_uint2(lo, hi);
+        sp[f * scale_row] = (uint8_t)sb;
+    }
+};
+
+// The Hadamard quantizer with noise sums: the grid is capped in y and each workgroup
+// strides over the chunk blocks of its feature block, so that few workgroups publish noise sums
+// (same-address fp64 atomics serialize).  Every thread reaches the workgroup reduction.
+template <typename T, bool kSR>
 __global__ void __launch_bounds__(kRhtThreads)
 k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
             const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
@@ -409,61 +391,187 @@ k_rht_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t
     fill_enc_table(tab, ts);
     const uint32_t mask = rht_sign_mask(sign_seed);
     double g2 = 0.0, e2 = 0.0;
-    if constexpr (kNoise) {
-        // The grid is capped in y and each workgroup strides over the chunk blocks of its
-        // feature block, so that few workgroups publish noise sums (same-address fp64 atomics
-        // serialize).  Every thread reaches the workgroup reduction.
-        for (uint32_t by = blockIdx.y; by < chunk_blocks; by += gridDim.y) {
-            const RhtCoords rc = rht_coords_at(Tn, F, blockIdx.x, by);
-            if (rc.valid) {
-                Tile16x8<T> tile;
-                tile.load(x + rc.c * 16 * ld + rc.f0, ld);
-                quant_tile_transposed<T, kSR, true>(tile, rc, Tn, F, mask, ts, tab, seed, codes,
-                                                    scales, g2, e2);
-            }
+    for (uint32_t by = blockIdx.y; by < chunk_blocks; by += gridDim.y) {
+        const RhtCoords rc = rht_coords_at(Tn, F, blockIdx.x, by);
+        if (rc.valid) {
+            Tile16x8<T> tile;
+            tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+            const GlobalColumnSink sink{codes + rc.f0 * (Tn / 2) + rc.c * 8,
+                                        scales + rc.f0 * (Tn / 16) + rc.c, Tn / 2, Tn / 16};
+            quant_tile_transposed<T, kSR, true>(tile, rc.f0, rc.c * 16, Tn, mask, ts, tab, seed,
+                                                g2, e2, sink);
         }
-        publish_noise<kRhtThreads>(g2, e2, ts, sums);
-    } else {
-        const RhtCoords rc = rht_coords(Tn, F);
-        if (!rc.valid) return;
-        Tile16x8<T> tile;
-        tile.load(x + rc.c * 16 * ld + rc.f0, ld);
-        quant_tile_transposed<T, kSR, false>(tile, rc, Tn, F, mask, ts, tab, seed, codes, scales,
-                                             g2, e2);
     }
+    publish_noise<kRhtThreads>(g2, e2, ts, sums);
 }
 
 // Fused dual-orientation quantizer: one read of x gives the row-wise copy [T x F] (as the 1D
 // quantizer makes it, element index row * F + col for SR) and the Hadamard-transformed
-// transposed copy [F x T] (as k_rht_quant makes it, element index feature * T + token).
-template <typename T, bool kSR>
-__global__ void __launch_bounds__(kRhtThreads)
+// transposed copy [F x T] (as k_rht_quant makes it, element index feature * T + token).  With
+// kRows false it makes the transposed copy alone (the Hadamard quantizer without noise sums).
+//
+// A workgroup of 2 kTok threads takes a tile of 256 features x kTok tokens.  Thread (fg, ch) =
+// (lane % 32, 2 * wave + lane / 32) owns features 8 fg .. 8 fg + 7 of the 16 tokens of chunk ch,
+// so that each load instruction of a wave reads 512 contiguous bytes of two token rows.  Both
+// copies are staged in LDS and leave as whole rows of the tile: 128 code bytes and 16 scale
+// bytes for each of its kTok token rows, kTok / 2 code bytes and kTok / 16 scale bytes for each
+// of its 256 feature rows.  Stored straight from the threads, the transposed copy would leave as
+// 8-byte code pieces and single scale bytes of 32 feature rows per store instruction (one memory
+// request per piece), and took longer than reading the input.
+constexpr int kDualFeat = 256;
+
+template <int kTok, bool kRows>
+struct DualStage {
+    uint32_t cols[kDualFeat * kTok / 8];     // transposed codes (col_slot)
+    uint8_t csc[kDualFeat * (kTok / 16)];    // transposed scale bytes [feature row][chunk]
+    uint32_t rows[kRows ? kTok * 32 : 1];    // row-wise codes, 32 words per token row (row_slot)
+    uint8_t rsc[kRows ? kTok * 16 : 1];      // row-wise scale bytes [token row][feature block]
+};
+
+// LDS word of token row r: rows with bit 4 set trade places with their neighbour, so that the
+// two chunks a wave writes (rows r and r + 16) fall in opposite halves of the 64 banks.
+__device__ __forceinline__ uint32_t row_slot(uint32_t r) { return (r ^ ((r >> 4) & 1u)) * 32u; }
+
+// LDS word of 8-byte piece q (chunk q) of transposed feature row p, with P = kTok / 8 words per
+// row (64 / P rows per pass over the 64 banks) and P / 2 pieces: the row's position within its
+// group of 64 / P rows is XORed with bits of p / 8 and its pieces are XOR-permuted by the next
+// bits of p / 8, so that the 32 lanes of a half-wave writing one feature of 32 feature groups,
+// and the lanes reading whole consecutive rows, each cover all 64 banks.
+template <int kTok>
+__device__ __forceinline__ uint32_t col_slot(uint32_t p, uint32_t q) {
+    constexpr uint32_t P = kTok / 8, R = 64 / P, Q = P / 2;
+    const uint32_t g = p >> 3;
+    return (p ^ (g & (R - 1))) * P + 2u * (q ^ ((g / R) & (Q - 1)));
+}
+
+// Tile of workgroup w of a 1D grid of n tiles, gx of them across the features.  Workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2, so workgroup w runs on XCD
+// w % 8; tile (w % 8) * (n / 8) + w / 8 gives every XCD a contiguous range of tiles, i.e. runs
+// of adjacent feature tiles of the same tokens, whose row-wise scale bytes share lines.
+// n % 8 != 0: tile w.
+__device__ __forceinline__ void dual_tile(uint32_t gx, uint32_t& bx, uint32_t& by) {
+    const uint32_t w = blockIdx.x, n = gridDim.x;
+    const uint32_t t = (n & 7u) == 0 ? (w & 7u) * (n >> 3) + (w >> 3) : w;
+    by = t / gx;
+    bx = t - by * gx;
+}
+
+// At most 128 VGPRs (4 waves per SIMD) for bf16 input; the fp32 tile holds twice the registers.
+template <typename T> constexpr int dual_min_waves() { return sizeof(T) == 2 ? 4 : 2; }
+
+// Tokens per tile, measured on 16384 x 20480 and 16384 x 5120 bf16 tensors: 256 for round to
+// nearest (store-bound: fewer, wider row pieces), 128 for stochastic rounding (ALU-bound: more
+// workgroups per CU overlap one's stores with another's arithmetic).
+template <bool kSR> constexpr int dual_tile_tokens() { return kSR ? 128 : 256; }
+
+template <typename T, bool kSR, bool kRows>
+__global__ void __launch_bounds__(2 * dual_tile_tokens<kSR>(), dual_min_waves<T>())
 k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
              const float* __restrict__ amax_src, const float* __restrict__ amax_t_src,
              uint64_t seed, uint64_t seed_t, uint8_t* __restrict__ codes,
              uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
              uint8_t* __restrict__ scales_t, float* amax_out, float* sdec_out, float* amax_t_out,
              float* sdec_t_out) {
-    const float A = *amax_src, At = *amax_t_src;
-    const TensorScales ts = tensor_scales(A), tst = tensor_scales(At);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-        *amax_out = A;
-        *sdec_out = ts.s_dec;
+    constexpr int kTok = dual_tile_tokens<kSR>();
+    constexpr uint32_t kThreads = 2 * kTok, kPieces = kTok / 16;
+    const float At = *amax_t_src;
+    const TensorScales tst = tensor_scales(At);
+    TensorScales ts = tst;
+    if constexpr (kRows) ts = tensor_scales(*amax_src);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if constexpr (kRows) {
+            *amax_out = *amax_src;
+            *sdec_out = ts.s_dec;
+        }
         *amax_t_out = At;
         *sdec_t_out = tst.s_dec;
     }
     __shared__ EncTable tab, tab_t;
-    fill_enc_table(tab, ts);
+    __shared__ DualStage<kTok, kRows> stg;
+    if constexpr (kRows) fill_enc_table(tab, ts);
     fill_enc_table(tab_t, tst);
-    const RhtCoords rc = rht_coords_xcd(Tn, F);
-    if (!rc.valid) return;
-    const uint32_t mask = rht_sign_mask(sign_seed);
-    Tile16x8<T> tile;
-    tile.load(x + rc.c * 16 * ld + rc.f0, ld);
-    quant_tile_rows<T, kSR>(tile, rc, F, ts, tab, seed, codes, scales);
-    double g2 = 0.0, e2 = 0.0;             // unused: the dual quantizer has no noise sums
-    quant_tile_transposed<T, kSR, false>(tile, rc, Tn, F, mask, tst, tab_t, seed_t, codes_t,
-                                         scales_t, g2, e2);
+    uint32_t bx, by;
+    dual_tile((uint32_t)((F + kDualFeat - 1) / kDualFeat), bx, by);
+    const int64_t tf = (int64_t)bx * kDualFeat, tt = (int64_t)by * kTok;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t fg = lane & 31u, ch = 2u * (threadIdx.x >> 6) + (lane >> 5);
+    const int64_t f0 = tf + fg * 8, row0 = tt + ch * 16;
+    if (f0 < F && row0 < Tn) {
+        Tile16x8<T> tile;
+        tile.load(x + row0 * ld + f0, ld);
+        if constexpr (kRows)
+            quant_tile_rows<T, kSR>(tile, f0, row0, F, ts, tab, seed,
+                                    [&](int i, uint32_t packed, uint32_t sb) {
+                                        const uint32_t r = ch * 16 + (uint32_t)i;
+                                        stg.rows[row_slot(r) + fg] = packed;
+                                        if ((fg & 1u) == 0)
+                                            stg.rsc[r * 16 + (fg >> 1)] = (uint8_t)sb;
+                                    });
+        double g2 = 0.0, e2 = 0.0;             // unused: no noise sums here
+        quant_tile_transposed<T, kSR, false>(
+            tile, f0, row0, Tn, rht_sign_mask(sign_seed), tst, tab_t, seed_t, g2, e2,
+            [&](int f, uint32_t lo, uint32_t hi, uint32_t sb) {
+                const uint32_t p = fg * 8 + (uint32_t)f;
+                *reinterpret_cast<uint2*>(&stg.cols[col_slot<kTok>(p, ch)]) = make_uint2(lo, hi);
+                stg.csc[p * kPieces + ch] = (uint8_t)sb;
+            });
+    }
+    __syncthreads();
+    // Codes: 8 bytes per lane (16 tokens or 16 features), whole rows of the tile per wave
+    // instruction.  F % 16 == 0 and T % 16 == 0 keep every piece whole and 8-byte aligned.
+    // Scales: 4-byte words (four blocks) when the row length in blocks is a multiple of 4 (then
+    // a word is wholly inside or outside the matrix), else single bytes.
+#pragma unroll 2
+    for (uint32_t j = threadIdx.x; j < kDualFeat * kPieces; j += kThreads) {
+        const uint32_t p = j / kPieces, q = j % kPieces;
+        if (tf + p < F && tt + q * 16 < Tn)
+            *reinterpret_cast<uint2*>(codes_t + (tf + p) * (Tn / 2) + tt / 2 + q * 8) =
+                *reinterpret_cast<const uint2*>(&stg.cols[col_slot<kTok>(p, q)]);
+    }
+    if (Tn % 64 == 0) {
+        for (uint32_t j = threadIdx.x; j < kDualFeat * kPieces / 4; j += kThreads) {
+            const uint32_t p = j / (kPieces / 4), d = j % (kPieces / 4);
+            if (tf + p < F && tt + d * 64 < Tn)
+                *reinterpret_cast<uint32_t*>(scales_t + (tf + p) * (Tn / 16) + tt / 16 + d * 4) =
+                    *reinterpret_cast<const uint32_t*>(&stg.csc[p * kPieces + d * 4]);
+        }
+    } else {
+        for (uint32_t j = threadIdx.x; j < kDualFeat * kPieces; j += kThreads) {
+            const uint32_t p = j / kPieces, b = j % kPieces;
+            if (tf + p < F && tt + b * 16 < Tn)
+                scales_t[(tf + p) * (Tn / 16) + tt / 16 + b] = stg.csc[p * kPieces + b];
+        }
+    }
+    if constexpr (kRows) {
+#pragma unroll 2
+        for (uint32_t j = threadIdx.x; j < kTok * 16; j += kThreads) {
+            const uint32_t r = j >> 4, q = j & 15u;
+            if (tt + r < Tn && tf + q * 16 < F)
+                *reinterpret_cast<uint2*>(codes + (tt + r) * (F / 2) + tf / 2 + q * 8) =
+                    *reinterpret_cast<const uint2*>(&stg.rows[row_slot(r) + 2 * q]);
+        }
+        if (F % 64 == 0) {
+            for (uint32_t j = threadIdx.x; j < kTok * 4; j += kThreads) {
+                const uint32_t r = j >> 2, d = j & 3u;
+                if (tt + r < Tn && tf + d * 64 < F)
+                    *reinterpret_cast<uint32_t*>(scales + (tt + r) * (F / 16) + tf / 16 + d * 4) =
+                        *reinterpret_cast<const uint32_t*>(&stg.rsc[r * 16 + d * 4]);
+            }
+        } else {
+            for (uint32_t j = threadIdx.x; j < kTok * 16; j += kThreads) {
+                const uint32_t r = j >> 4, b = j & 15u;
+                if (tt + r < Tn && tf + b * 16 < F)
+                    scales[(tt + r) * (F / 16) + tf / 16 + b] = stg.rsc[r * 16 + b];
+            }
+        }
+    }
+}
+
+// Workgroups of the staged quantizer for a T x F input, or -1 if the count reaches 2^31.
+static int64_t dual_grid(int64_t T, int64_t F, bool sr) {
+    const int64_t tok = sr ? dual_tile_tokens<true>() : dual_tile_tokens<false>();
+    const int64_t tiles = ((F + kDualFeat - 1) / kDualFeat) * ((T + tok - 1) / tok);
+    return tiles >= (1ll << 31) ? -1 : tiles;
 }
 
 // MXFP4 quantization of x^T [P3 NVFP4 in pratica: MXFP4, 32-element blocks with power-of-two
@@ -632,25 +740,38 @@ static nvfp4_status hadamard_quantize(const void* x, nvfp4_dtype dt, int64_t ld,
         hipLaunchKernelGGL(k_scalars_rht, dim3(1), dim3(1), 0, st, src, out->amax, out->s_dec);
         return launch_status();
     }
+    if (!sums) {
+        // the staged quantizer without its row-wise copy
+        const int64_t tiles = dual_grid(T, F, rnd == NVFP4_SR);
+        if (tiles < 0) return NVFP4_ERR_SHAPE;
+        const dim3 grid((uint32_t)tiles);
+#define NVFP4_RQ(TT, SRV)                                                                         \
+        hipLaunchKernelGGL((k_dual_quant<TT, SRV, false>), grid, dim3(2 * dual_tile_tokens<SRV>()), \
+                           0, st, static_cast<const TT*>(x), T, F, ld, sign_seed, nullptr, src,   \
+                           0, seed, nullptr, nullptr, out->codes, out->scales, nullptr, nullptr,  \
+                           out->amax, out->s_dec)
+        if (dt == NVFP4_BF16) {
+            if (rnd == NVFP4_SR) NVFP4_RQ(uint16_t, true); else NVFP4_RQ(uint16_t, false);
+        } else {
+            if (rnd == NVFP4_SR) NVFP4_RQ(float, true); else NVFP4_RQ(float, false);
+        }
+#undef NVFP4_RQ
+        return launch_status();
+    }
     dim3 grid = rht_grid(T, F);
     const uint32_t chunk_blocks = grid.y;
-    if (sums) {
-        const uint32_t cap = (kNoiseWorkgroups + grid.x - 1) / grid.x;
-        grid.y = chunk_blocks < cap ? chunk_blocks : cap;
-    }
+    const uint32_t cap = (kNoiseWorkgroups + grid.x - 1) / grid.x;
+    grid.y = chunk_blocks < cap ? chunk_blocks : cap;
     const dim3 block(kRhtThreads);
-#define NVFP4_RQ(TT, SRV, NZ)                                                                      \
-    hipLaunchKernelGGL((k_rht_quant<TT, SRV, NZ>), grid, block, 0, st, static_cast<const TT*>(x), T, \
+#define NVFP4_RQ(TT, SRV)                                                                         \
+    hipLaunchKernelGGL((k_rht_quant<TT, SRV>), grid, block, 0, st, static_cast<const TT*>(x), T,  \
                        F, ld, sign_seed, src, seed, out->codes, out->scales, out->amax, out->s_dec, \
                        sums, chunk_blocks)
-#define NVFP4_RQR(TT, NZ)                                                                          \
-    if (rnd == NVFP4_SR) NVFP4_RQ(TT, true, NZ); else NVFP4_RQ(TT, false, NZ)
     if (dt == NVFP4_BF16) {
-        if (sums) NVFP4_RQR(uint16_t, true); else NVFP4_RQR(uint16_t, false);
+        if (rnd == NVFP4_SR) NVFP4_RQ(uint16_t, true); else NVFP4_RQ(uint16_t, false);
     } else {
-        if (sums) NVFP4_RQR(float, true); else NVFP4_RQR(float, false);
+        if (rnd == NVFP4_SR) NVFP4_RQ(float, true); else NVFP4_RQ(float, false);
     }
-#undef NVFP4_RQR
 #undef NVFP4_RQ
     return launch_status();
 }
@@ -710,14 +831,14 @@ extern "C" nvfp4_status nvfp4_quantize_dual(const void* x, nvfp4_dtype dt, int64
         hipLaunchKernelGGL(k_scalars_rht, dim3(1), dim3(1), 0, st, src_t, out_t->amax, out_t->s_dec);
         return launch_status();
     }
-    const dim3 g2 = rht_grid(T, F), block(kRhtThreads);
-    if ((int64_t)g2.x * g2.y >= (1ll << 31)) return NVFP4_ERR_SHAPE;
-    const dim3 grid(g2.x * g2.y);              // tiles placed by rht_coords_xcd
+    const int64_t tiles = dual_grid(T, F, rnd == NVFP4_SR);
+    if (tiles < 0) return NVFP4_ERR_SHAPE;
+    const dim3 grid((uint32_t)tiles);         // tiles placed by dual_tile
 #define NVFP4_DQ(TT, SRV)                                                                         \
-    hipLaunchKernelGGL((k_dual_quant<TT, SRV>), grid, block, 0, st, static_cast<const TT*>(x), T, \
-                       F, ld, sign_seed, src, src_t, seed, seed_t, out->codes, out->scales,        \
-                       out_t->codes, out_t->scales, out->amax, out->s_dec, out_t->amax,            \
-                       out_t->s_dec)
+    hipLaunchKernelGGL((k_dual_quant<TT, SRV, true>), grid, dim3(2 * dual_tile_tokens<SRV>()), 0, \
+                       st, static_cast<const TT*>(x), T, F, ld, sign_seed, src, src_t, seed,      \
+                       seed_t, out->codes, out->scales, out_t->codes, out_t->scales, out->amax,   \
+                       out->s_dec, out_t->amax, out_t->s_dec)
     if (dt == NVFP4_BF16) {
         if (rnd == NVFP4_SR) NVFP4_DQ(uint16_t, true); else NVFP4_DQ(uint16_t, false);
     } else {

@@ -34,7 +34,11 @@ SHAPES = [("fp32_outliers", lambda: W.small_fp32((256, 256), 101)),
           ("bf16_act_ragged", lambda: W.act((48, 80), 5)),
           ("bf16_one_chunk", lambda: W.grad((16, 16), 6)),
           ("bf16_tiles_and_tail", lambda: W.act((528, 4096 + 48), 7)),
-          ("fp32_grad", lambda: W.grad((96, 160), 8).float())]
+          ("fp32_grad", lambda: W.grad((96, 160), 8).float()),
+          # 256 x 256 tiles: ragged tiles in both directions with whole-word scale stores
+          # (F % 64 == 0, T % 64 == 0), and 16 tiles placed XCD by XCD (count % 8 == 0)
+          ("bf16_ragged_tiles_word_scales", lambda: W.act((320, 576), 10)),
+          ("bf16_sixteen_tiles", lambda: W.grad((2048, 512), 11))]
 
 
 @pytest.mark.parametrize("name,make", SHAPES)
@@ -117,3 +121,15 @@ def test_dual_full_size_sampled(nv, orc, which):
     np.testing.assert_array_equal(qt.codes[:64].cpu().numpy(), ot["codes"])
     np.testing.assert_array_equal(qt.scales[:64].cpu().numpy(), ot["scales"])
     assert float(q.s_dec.item()) == o["s_dec"] and float(qt.s_dec.item()) == ot["s_dec"]
+    if rnd == 0:
+        # round to nearest depends on the values only: rows and features from the middle and
+        # the end of the tensor (other tiles, other XCD ranges) as well
+        for r0 in (8192 - 32, 16384 - 64):
+            o = orc.quantize_1d(np.ascontiguousarray(xb[r0:r0 + 64]), amax_in=A)
+            np.testing.assert_array_equal(q.codes[r0:r0 + 64].cpu().numpy(), o["codes"])
+            np.testing.assert_array_equal(q.scales[r0:r0 + 64].cpu().numpy(), o["scales"])
+        for f0 in (2048 - 128, 4096 - 64):
+            ot = orc.hadamard_quantize(np.ascontiguousarray(xb[:, f0:f0 + 64]), SIGN, 0, 0,
+                                       amax_in=At)
+            np.testing.assert_array_equal(qt.codes[f0:f0 + 64].cpu().numpy(), ot["codes"])
+            np.testing.assert_array_equal(qt.scales[f0:f0 + 64].cpu().numpy(), ot["scales"])

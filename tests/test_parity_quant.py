@@ -111,7 +111,7 @@ def test_quantize_2d_strided(nv, orc):
 
 
 @pytest.mark.parametrize("rounding", [0, 1])
-@pytest.mark.parametrize("T,F", [(48, 24), (512, 64), (528, 136)])
+@pytest.mark.parametrize("T,F", [(48, 24), (512, 64), (528, 136), (640, 264)])
 def test_hadamard_quantize_small(nv, orc, rounding, T, F):
     x = W.act((T, F), T + F)
     g = nv.hadamard_quantize(x.to(DEV), sign_seed=0x51E4, rounding=rounding, seed=5)
