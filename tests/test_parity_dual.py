@@ -133,3 +133,22 @@ def test_dual_full_size_sampled(nv, orc, which):
                                        amax_in=At)
             np.testing.assert_array_equal(qt.codes[f0:f0 + 64].cpu().numpy(), ot["codes"])
             np.testing.assert_array_equal(qt.scales[f0:f0 + 64].cpu().numpy(), ot["scales"])
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_dual_random_shapes(nv, orc, case):
+    """Seeded random shapes (T % 16 == 0, F % 16 == 0, up to 1200 x 800) through the staged
+    quantizer's ragged tiles, both roundings, against the oracle; and the plain Hadamard
+    quantizer (the same kernel without its row-wise copy) on F % 8 == 0 shapes."""
+    rng = np.random.default_rng(1000 + case)
+    T, F = 16 * int(rng.integers(1, 76)), 16 * int(rng.integers(1, 51))
+    rounding = case % 2
+    x = W.act((T, F), 2000 + case) if case % 4 < 2 else W.grad((T, F), 2000 + case)
+    q, qt = nv.quantize_dual(x.to(DEV), SIGN, rounding, seed=case, seed_t=case + 100)
+    xb = W.bits(x)
+    _same_q(q, orc.quantize_1d(xb, rounding=rounding, seed=case), f"{T}x{F} rows")
+    _same_q(qt, orc.hadamard_quantize(xb, SIGN, rounding, case + 100), f"{T}x{F} transposed")
+    F8 = 8 * int(rng.integers(1, 101))
+    x8 = W.act((T, F8), 3000 + case)
+    g = nv.hadamard_quantize(x8.to(DEV), sign_seed=SIGN, rounding=rounding, seed=case)
+    _same_q(g, orc.hadamard_quantize(W.bits(x8), SIGN, rounding, case), f"rht {T}x{F8}")
