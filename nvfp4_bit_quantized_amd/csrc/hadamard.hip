@@ -172,10 +172,6 @@ __device__ __forceinline__ RhtCoords rht_coords_at(int64_t T, int64_t F, uint32_
     return rc;
 }
 
-__device__ __forceinline__ RhtCoords rht_coords(int64_t T, int64_t F) {
-    return rht_coords_at(T, F, blockIdx.x, blockIdx.y);
-}
-
 // Persistent over (64-feature x 512-token) tiles, at most kRhtAmaxBlocks workgroups, each
 // publishing its maximum once (publish_amax).  The factor 1/4 of the transform is applied to the
 // maximum instead of to every element: scaling by 1/4 and fp32 rounding are both monotonic, so
@@ -464,6 +460,48 @@ template <typename T> constexpr int dual_min_waves() { return sizeof(T) == 2 ? 4
 // workgroups per CU overlap one's stores with another's arithmetic).
 template <bool kSR> constexpr int dual_tile_tokens() { return kSR ? 128 : 256; }
 
+// Write-out of a staged tile (every thread of the workgroup calls these after the barrier).
+// Transposed codes: 256 feature rows x kTok / 2 bytes, 8 bytes (16 tokens) per lane, whole rows
+// of the tile per wave instruction; T % 16 == 0 keeps every piece whole and 8-byte aligned.
+template <int kTok>
+__device__ __forceinline__ void write_staged_cols(const uint32_t* cols, uint8_t* __restrict__ codes_t,
+                                                  int64_t tf, int64_t tt, int64_t F, int64_t Tn) {
+    constexpr uint32_t kThreads = 2 * kTok, kPieces = kTok / 16;
+#pragma unroll 2
+    for (uint32_t j = threadIdx.x; j < kDualFeat * kPieces; j += kThreads) {
+        const uint32_t p = j / kPieces, q = j % kPieces;
+        if (tf + p < F && tt + q * 16 < Tn)
+            *reinterpret_cast<uint2*>(codes_t + (tf + p) * (Tn / 2) + tt / 2 + q * 8) =
+                *reinterpret_cast<const uint2*>(&cols[col_slot<kTok>(p, q)]);
+    }
+}
+
+// Scale bytes staged as `rows` rows of `per_row` bytes, going to rows r0 .. of a matrix with
+// rows_total rows of row_len bytes, from byte col0 (a multiple of per_row).  4-byte words when
+// row_len and per_row are multiples of 4 (then a word is wholly inside or outside the matrix),
+// else single bytes.
+template <uint32_t kThreads>
+__device__ __forceinline__ void write_staged_scales(const uint8_t* stage, uint32_t rows,
+                                                    uint32_t per_row, uint8_t* __restrict__ dst,
+                                                    int64_t row_len, int64_t r0,
+                                                    int64_t rows_total, int64_t col0) {
+    if (row_len % 4 == 0 && per_row % 4 == 0) {
+        const uint32_t words = per_row / 4;
+        for (uint32_t j = threadIdx.x; j < rows * words; j += kThreads) {
+            const uint32_t r = j / words, d = j % words;
+            if (r0 + r < rows_total && col0 + 4 * d < row_len)
+                *reinterpret_cast<uint32_t*>(dst + (r0 + r) * row_len + col0 + 4 * d) =
+                    *reinterpret_cast<const uint32_t*>(&stage[r * per_row + 4 * d]);
+        }
+    } else {
+        for (uint32_t j = threadIdx.x; j < rows * per_row; j += kThreads) {
+            const uint32_t r = j / per_row, b = j % per_row;
+            if (r0 + r < rows_total && col0 + b < row_len)
+                dst[(r0 + r) * row_len + col0 + b] = stage[r * per_row + b];
+        }
+    }
+}
+
 template <typename T, bool kSR, bool kRows>
 __global__ void __launch_bounds__(2 * dual_tile_tokens<kSR>(), dual_min_waves<T>())
 k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
@@ -517,32 +555,10 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
             });
     }
     __syncthreads();
-    // Codes: 8 bytes per lane (16 tokens or 16 features), whole rows of the tile per wave
-    // instruction.  F % 16 == 0 and T % 16 == 0 keep every piece whole and 8-byte aligned.
-    // Scales: 4-byte words (four blocks) when the row length in blocks is a multiple of 4 (then
-    // a word is wholly inside or outside the matrix), else single bytes.
-#pragma unroll 2
-    for (uint32_t j = threadIdx.x; j < kDualFeat * kPieces; j += kThreads) {
-        const uint32_t p = j / kPieces, q = j % kPieces;
-        if (tf + p < F && tt + q * 16 < Tn)
-            *reinterpret_cast<uint2*>(codes_t + (tf + p) * (Tn / 2) + tt / 2 + q * 8) =
-                *reinterpret_cast<const uint2*>(&stg.cols[col_slot<kTok>(p, q)]);
-    }
-    if (Tn % 64 == 0) {
-        for (uint32_t j = threadIdx.x; j < kDualFeat * kPieces / 4; j += kThreads) {
-            const uint32_t p = j / (kPieces / 4), d = j % (kPieces / 4);
-            if (tf + p < F && tt + d * 64 < Tn)
-                *reinterpret_cast<uint32_t*>(scales_t + (tf + p) * (Tn / 16) + tt / 16 + d * 4) =
-                    *reinterpret_cast<const uint32_t*>(&stg.csc[p * kPieces + d * 4]);
-        }
-    } else {
-        for (uint32_t j = threadIdx.x; j < kDualFeat * kPieces; j += kThreads) {
-            const uint32_t p = j / kPieces, b = j % kPieces;
-            if (tf + p < F && tt + b * 16 < Tn)
-                scales_t[(tf + p) * (Tn / 16) + tt / 16 + b] = stg.csc[p * kPieces + b];
-        }
-    }
+    write_staged_cols<kTok>(stg.cols, codes_t, tf, tt, F, Tn);
+    write_staged_scales<kThreads>(stg.csc, kDualFeat, kPieces, scales_t, Tn / 16, tf, F, tt / 16);
     if constexpr (kRows) {
+        // row-wise codes: 16 lanes per token row, 8 bytes (16 features) each; F % 16 == 0
 #pragma unroll 2
         for (uint32_t j = threadIdx.x; j < kTok * 16; j += kThreads) {
             const uint32_t r = j >> 4, q = j & 15u;
@@ -550,20 +566,7 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
                 *reinterpret_cast<uint2*>(codes + (tt + r) * (F / 2) + tf / 2 + q * 8) =
                     *reinterpret_cast<const uint2*>(&stg.rows[row_slot(r) + 2 * q]);
         }
-        if (F % 64 == 0) {
-            for (uint32_t j = threadIdx.x; j < kTok * 4; j += kThreads) {
-                const uint32_t r = j >> 2, d = j & 3u;
-                if (tt + r < Tn && tf + d * 64 < F)
-                    *reinterpret_cast<uint32_t*>(scales + (tt + r) * (F / 16) + tf / 16 + d * 4) =
-                        *reinterpret_cast<const uint32_t*>(&stg.rsc[r * 16 + d * 4]);
-            }
-        } else {
-            for (uint32_t j = threadIdx.x; j < kTok * 16; j += kThreads) {
-                const uint32_t r = j >> 4, b = j & 15u;
-                if (tt + r < Tn && tf + b * 16 < F)
-                    scales[(tt + r) * (F / 16) + tf / 16 + b] = stg.rsc[r * 16 + b];
-            }
-        }
+        write_staged_scales<kThreads>(stg.rsc, kTok, 16, scales, F / 16, tt, Tn, tf / 16);
     }
 }
 
@@ -575,52 +578,66 @@ static int64_t dual_grid(int64_t T, int64_t F, bool sr) {
 }
 
 // MXFP4 quantization of x^T [P3 NVFP4 in pratica: MXFP4, 32-element blocks with power-of-two
-// scales, is the comparison format]: the 32 tokens of block b of feature f are chunks 2b and
-// 2b + 1, held by lanes l and l ^ 8 of one wave; the block amax is shared with one lane
-// exchange, E8M0 exponent floor(log2 amax) - 2 clamped to [-127, 127] (0 for an all-zero
-// block), codes E2M1 of x * 2^-exponent (RNE, or SR with element index f * T + t), each lane
-// writing its 8 code bytes and the even-chunk lane the scale byte.  T % 32 == 0, so both lanes
-// of a pair are valid or neither is.
+// scales, is the comparison format], on the staged quantizer's tiles (256 features x kTok
+// tokens, 2 kTok threads): the 32 tokens of block b of a feature are chunks 2b and 2b + 1, held
+// by lanes l and l + 32 of one wave; the block amax is shared with one lane exchange, E8M0
+// exponent floor(log2 amax) - 2 clamped to [-127, 127] (0 for an all-zero block), codes E2M1 of
+// x * 2^-exponent (RNE, or SR with element index f * T + t).  Codes and scale bytes are staged
+// in LDS and leave as whole tile rows.  T % 32 == 0, so both lanes of a pair are valid or
+// neither is.
 template <typename T, bool kSR>
-__global__ void __launch_bounds__(kRhtThreads)
+__global__ void __launch_bounds__(2 * dual_tile_tokens<kSR>(), dual_min_waves<T>())
 k_mx_quant_t(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t seed,
              uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-    const RhtCoords rc = rht_coords(Tn, F);
-    if (!rc.valid) return;
-    Tile16x8<T> tile;
-    tile.load(x + rc.c * 16 * ld + rc.f0, ld);
+    constexpr int kTok = dual_tile_tokens<kSR>();
+    constexpr uint32_t kThreads = 2 * kTok, kBlocks = kTok / 32;
+    __shared__ uint32_t cols[kDualFeat * kTok / 8];
+    __shared__ uint8_t csc[kDualFeat * kBlocks];
+    uint32_t bx, by;
+    dual_tile((uint32_t)((F + kDualFeat - 1) / kDualFeat), bx, by);
+    const int64_t tf = (int64_t)bx * kDualFeat, tt = (int64_t)by * kTok;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t fg = lane & 31u, ch = 2u * (threadIdx.x >> 6) + (lane >> 5);
+    const int64_t f0 = tf + fg * 8, row0 = tt + ch * 16;
+    if (f0 < F && row0 < Tn) {
+        Tile16x8<T> tile;
+        tile.load(x + row0 * ld + f0, ld);
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-        const int64_t feat = rc.f0 + f;
-        float v[16];
+        for (int f = 0; f < 8; ++f) {
+            float v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
-        float m = 0.0f;
+            for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
+            float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-        m = fmaxf(m, __shfl_xor(m, 8));
-        int e8 = 0;
-        if (m > 0.0f) {
-            e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
-            e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            int e8 = 0;
+            if (m > 0.0f) {
+                e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
+                e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
+            }
+            float z[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) z[e] = __builtin_amdgcn_ldexpf(v[e], -e8);
+            uint32_t lo, hi;
+            if constexpr (kSR) {
+                const uint64_t idx = (uint64_t)(f0 + f) * (uint64_t)Tn + (uint64_t)row0;
+                const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
+                const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+                lo = e2m1_sr_pack8(z, a);
+                hi = e2m1_sr_pack8(z + 8, b);
+            } else {
+                lo = e2m1_rne_pack8(z);
+                hi = e2m1_rne_pack8(z + 8);
+            }
+            const uint32_t p = fg * 8 + (uint32_t)f;
+            *reinterpret_cast<uint2*>(&cols[col_slot<kTok>(p, ch)]) = make_uint2(lo, hi);
+            if ((ch & 1u) == 0) csc[p * kBlocks + ch / 2] = (uint8_t)(e8 + 127);
         }
-        float z[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) z[e] = __builtin_amdgcn_ldexpf(v[e], -e8);
-        uint32_t lo, hi;
-        if constexpr (kSR) {
-            const uint64_t idx = (uint64_t)feat * (uint64_t)Tn + (uint64_t)rc.c * 16;
-            const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
-            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
-            lo = e2m1_sr_pack8(z, a);
-            hi = e2m1_sr_pack8(z + 8, b);
-        } else {
-            lo = e2m1_rne_pack8(z);
-            hi = e2m1_rne_pack8(z + 8);
-        }
-        *reinterpret_cast<uint2*>(codes + feat * (Tn / 2) + rc.c * 8) = make_uint2(lo, hi);
-        if ((rc.c & 1) == 0) scales[feat * (Tn / 32) + rc.c / 2] = (uint8_t)(e8 + 127);
     }
+    __syncthreads();
+    write_staged_cols<kTok>(cols, codes, tf, tt, F, Tn);
+    write_staged_scales<kThreads>(csc, kDualFeat, kBlocks, scales, Tn / 32, tf, F, tt / 32);
 }
 
 static dim3 rht_grid(int64_t T, int64_t F) {
@@ -859,11 +876,15 @@ extern "C" nvfp4_status mxfp4_quantize_1d_t(const void* x, nvfp4_dtype dt, int64
     if (T % 32 != 0) return NVFP4_ERR_SHAPE;
     if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
     if (T == 0 || F == 0) return NVFP4_OK;
-    const dim3 grid = rht_grid(T, F), block(kRhtThreads);
     hipStream_t st = as_stream(stream);
 #define NVFP4_MXT(TT, SRV)                                                                        \
-    hipLaunchKernelGGL((k_mx_quant_t<TT, SRV>), grid, block, 0, st, static_cast<const TT*>(x), T, \
-                       F, ld, seed, out->codes, out->scales)
+    do {                                                                                          \
+        const int64_t tiles = dual_grid(T, F, SRV);                                               \
+        if (tiles < 0) return NVFP4_ERR_SHAPE;                                                    \
+        hipLaunchKernelGGL((k_mx_quant_t<TT, SRV>), dim3((uint32_t)tiles),                        \
+                           dim3(2 * dual_tile_tokens<SRV>()), 0, st, static_cast<const TT*>(x),   \
+                           T, F, ld, seed, out->codes, out->scales);                              \
+    } while (0)
     if (dt == NVFP4_BF16) {
         if (rnd == NVFP4_SR) NVFP4_MXT(uint16_t, true); else NVFP4_MXT(uint16_t, false);
     } else {
