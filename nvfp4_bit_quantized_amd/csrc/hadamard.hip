@@ -9,12 +9,14 @@
 //
 // Thread mapping: a thread owns 8 consecutive features (one 16-byte bf16 load per token row)
 // and one 16-token chunk, so it holds the 16x8 input tile in registers and runs 8 independent
-// 16-point fast Walsh-Hadamard transforms.  A wave covers 8 feature groups (64 features, full
-// 128-byte rows on the read side) x 8 consecutive chunks (64 contiguous code bytes per feature
-// on the write side).
+// 16-point fast Walsh-Hadamard transforms.  The quantizers (k_dual_quant, k_mx_quant_t) place
+// 32 feature groups side by side in a wave (256 features: 512-byte reads of two token rows per
+// load), stage their results in LDS and write whole tile rows.  The quantizer with noise sums
+// (k_rht_quant) keeps the direct mapping of 8 feature groups x 8 chunks per wave and stores
+// from the threads.
 //
-// The same tiling also serves the transposing MXFP4 quantizer of the comparison format (no
-// transform; 32-token blocks made of two adjacent chunks held by lanes l and l ^ 8).
+// The staged tiling also serves the transposing MXFP4 quantizer of the comparison format (no
+// transform; 32-token blocks made of two adjacent chunks held by lanes l and l + 32).
 
 #include "device_codecs.hpp"
 #include "host_util.hpp"
@@ -182,9 +184,8 @@ __device__ __forceinline__ RhtCoords rht_coords_at(int64_t T, int64_t F, uint32_
 // valid token chunk / feature group / tile: the duplicates they read leave a maximum unchanged, so
 // every load is unconditional.  With kPlain the same pass also takes the amax of x itself (for
 // the fused dual-orientation quantizer).
-// The amax tiles are wider than the quantizer's: 256 features x 8 chunks per 256 threads (a wave
-// reads 512 contiguous bytes of each of two token rows per load, instead of 128 bytes of eight),
-// which suits HBM better; the quantizer keeps 64-feature tiles for its feature-major stores.
+// The amax tiles are 256 features x 8 chunks per 256 threads: a wave reads 512 contiguous bytes
+// of each of two token rows per load (instead of 128 bytes of eight), which suits HBM better.
 constexpr int kRhtAmaxBlocks = 256;
 constexpr int kAmaxFeat = 256, kAmaxChunks = 8;
 template <typename T> constexpr int rht_amax_sub() { return 2; }
