@@ -243,3 +243,14 @@ def test_binding_refuses_host_tensors():
         nv._ptr(x)
     with pytest.raises(ValueError):
         nv.quantize_1d(x)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every call raises; there is no fallback path."""
+    import torch
+    monkeypatch.setattr(nv, "LIB_PATH", str(tmp_path / "libnvfp4.so"))
+    monkeypatch.setattr(nv, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        nv.lib()
+    with pytest.raises((RuntimeError, ValueError)):
+        nv.quantize_1d(torch.zeros((16, 32), dtype=torch.bfloat16))
