@@ -293,6 +293,17 @@ NVFP4_API nvfp4_status mxfp4_quantize_1d(const void *x, nvfp4_dtype dt, int64_t 
 NVFP4_API nvfp4_status mxfp4_quantize_1d_t(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
                                            uint64_t seed, const nvfp4_tensor *out, void *stream);
 
+/* Both MXFP4 copies of x from one read, for the MXFP4 comparison [P3 NVFP4 in pratica]: x [T x F]
+ * (row stride ld) gives out [T x F] (out->rows = T, out->cols = F), the same bytes as
+ * mxfp4_quantize_1d(x, rnd, seed), and out_t [F x T], the same bytes as
+ * mxfp4_quantize_1d_t(x, rnd, seed_t).  Both tensors caller-owned, layout MXFP4_BLK_1x32.
+ * T % 32 == 0 and F % 32 == 0 (else NVFP4_ERR_SHAPE); the workgroup count
+ * ceil(F / 256) * ceil(T / 256) (RNE) or ceil(F / 256) * ceil(T / 128) (SR) must stay below
+ * 2^31, and the token-major limits above apply. */
+NVFP4_API nvfp4_status mxfp4_quantize_dual(const void *x, nvfp4_dtype dt, int64_t ld, nvfp4_round rnd,
+                                           uint64_t seed, uint64_t seed_t, const nvfp4_tensor *out,
+                                           const nvfp4_tensor *out_t, void *stream);
+
 /* MXFP4 x MXFP4 GEMM, C = A * B^T with fp32 accumulation, both operands MXFP4_BLK_1x32, stored
  * fp32 or bf16 (round to nearest even) into c [M x N] with row stride ldc.  Requirements as for
  * nvfp4_gemm with K % 32 == 0 (s_dec and amax are not used); K == 0 writes zeros. */

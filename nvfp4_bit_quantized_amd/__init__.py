@@ -26,7 +26,7 @@ SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_qu
            "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t", "nvfp4_amax_accumulate",
            "nvfp4_hadamard_amax_accumulate", "nvfp4_hadamard_quantize_noise", "nvfp4_gemm_ws",
            "nvfp4_gemm_workspace_size", "nvfp4_gemm_ws_noalloc", "mxfp4_gemm_ws",
-           "mxfp4_gemm_workspace_size")
+           "mxfp4_gemm_workspace_size", "mxfp4_quantize_dual")
 
 
 class NvTensor(C.Structure):
@@ -68,6 +68,7 @@ def lib():
         L.mxfp4_quantize_1d.argtypes = [P, i32, i64, i32, u64, T, P]
         L.mxfp4_gemm.argtypes = [T, T, P, i32, i64, P]
         L.mxfp4_quantize_1d_t.argtypes = [P, i32, i64, i32, u64, T, P]
+        L.mxfp4_quantize_dual.argtypes = [P, i32, i64, i32, u64, u64, T, T, P]
         L.nvfp4_dual_amax.argtypes = [P, i32, i64, i64, i64, u64, P, P, P]
         L.nvfp4_quantize_dual.argtypes = [P, i32, i64, u64, P, P, i32, u64, u64, T, T, P]
         L.nvfp4_quantize_1d_noise.argtypes = [P, i32, i64, P, i32, u64, T, P, P]
@@ -355,6 +356,20 @@ def mx_quantize_1d_t(x: torch.Tensor, rounding: int = RNE, seed: int = 0,
     _check("mxfp4_quantize_1d_t", lib().mxfp4_quantize_1d_t(_ptr(x), dt, ld, rounding, seed,
                                                             C.byref(d), _stream(x.device)))
     return q
+
+
+def mx_quantize_dual(x: torch.Tensor, rounding: int = RNE, seed: int = 0, seed_t: int = 0,
+                     out: QTensor | None = None, out_t: QTensor | None = None):
+    """x [T x F] -> (row-wise MXFP4 [T x F], MXFP4 of x^T [F x T]) from one read."""
+    x, dt, ld = _x(x)
+    T, F = x.shape
+    q = QTensor.empty(T, F, MX_1x32, x.device) if out is None else out
+    qt = QTensor.empty(F, T, MX_1x32, x.device) if out_t is None else out_t
+    d, dt_ = q.desc(), qt.desc()
+    _check("mxfp4_quantize_dual",
+           lib().mxfp4_quantize_dual(_ptr(x), dt, ld, rounding, seed, seed_t, C.byref(d),
+                                     C.byref(dt_), _stream(x.device)))
+    return q, qt
 
 
 def mx_gemm_workspace_size(M: int, N: int, K: int) -> int:

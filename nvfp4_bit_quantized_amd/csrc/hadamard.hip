@@ -50,6 +50,13 @@ template <> struct Tile16x8<uint16_t> {
             w[i].x ^= s; w[i].y ^= s; w[i].z ^= s; w[i].w ^= s;
         }
     }
+    // No instruction: the words are marked as changed, so that values unpacked before this point
+    // are not kept live to be reused after it (the tile is smaller packed than unpacked).
+    __device__ __forceinline__ void fence() {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            asm volatile("" : "+v"(w[i].x), "+v"(w[i].y), "+v"(w[i].z), "+v"(w[i].w));
+    }
 };
 
 template <> struct Tile16x8<float> {
@@ -75,6 +82,7 @@ template <> struct Tile16x8<float> {
             for (int k = 0; k < 8; ++k) *e[k] = __uint_as_float(__float_as_uint(*e[k]) ^ s);
         }
     }
+    __device__ __forceinline__ void fence() {}
 };
 
 // Sign mask: bit j set <=> d_j = -1.  Word 0 of Philox4x32-10(key = sign_seed, counter = 0).
@@ -578,6 +586,56 @@ static int64_t dual_grid(int64_t T, int64_t F, bool sr) {
     return tiles >= (1ll << 31) ? -1 : tiles;
 }
 
+// E8M0 exponent of an MXFP4 block with maximum m: floor(log2 m) - 2 clamped to [-127, 127],
+// 0 for an all-zero block.
+__device__ __forceinline__ int mx_exponent(float m) {
+    int e8 = 0;
+    if (m > 0.0f) {
+        e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
+        e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
+    }
+    return e8;
+}
+
+// The transposed MXFP4 copy of one thread's tile into the LDS stage (kTok-token tiles): for
+// each of its 8 features, its 16 tokens are one half of a 32-token block whose other half sits
+// in lane l + 32 (the next chunk); codes to cols (col_slot), the scale byte from the even chunk
+// to csc.  SR element index feature * T + token.
+template <typename T, bool kSR, int kTok = dual_tile_tokens<kSR>()>
+__device__ __forceinline__ void mx_tile_transposed(const Tile16x8<T>& tile, int64_t f0, int64_t row0,
+                                                   int64_t Tn, uint64_t seed, uint32_t fg,
+                                                   uint32_t ch, uint32_t* cols, uint8_t* csc) {
+    constexpr uint32_t kBlocks = kTok / 32;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const int e8 = mx_exponent(m);
+        float z[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) z[e] = __builtin_amdgcn_ldexpf(v[e], -e8);
+        uint32_t lo, hi;
+        if constexpr (kSR) {
+            const uint64_t idx = (uint64_t)(f0 + f) * (uint64_t)Tn + (uint64_t)row0;
+            const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
+            const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
+            lo = e2m1_sr_pack8(z, a);
+            hi = e2m1_sr_pack8(z + 8, b);
+        } else {
+            lo = e2m1_rne_pack8(z);
+            hi = e2m1_rne_pack8(z + 8);
+        }
+        const uint32_t p = fg * 8 + (uint32_t)f;
+        *reinterpret_cast<uint2*>(&cols[col_slot<kTok>(p, ch)]) = make_uint2(lo, hi);
+        if ((ch & 1u) == 0) csc[p * kBlocks + ch / 2] = (uint8_t)(e8 + 127);
+    }
+}
+
 // MXFP4 quantization of x^T [P3 NVFP4 in pratica: MXFP4, 32-element blocks with power-of-two
 // scales, is the comparison format], on the staged quantizer's tiles (256 features x kTok
 // tokens, 2 kTok threads): the 32 tokens of block b of a feature are chunks 2b and 2b + 1, held
@@ -603,42 +661,81 @@ k_mx_quant_t(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
     if (f0 < F && row0 < Tn) {
         Tile16x8<T> tile;
         tile.load(x + row0 * ld + f0, ld);
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            float v[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = tile.get(i, f);
-            float m = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            int e8 = 0;
-            if (m > 0.0f) {
-                e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
-                e8 = e8 < -127 ? -127 : (e8 > 127 ? 127 : e8);
-            }
-            float z[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) z[e] = __builtin_amdgcn_ldexpf(v[e], -e8);
-            uint32_t lo, hi;
-            if constexpr (kSR) {
-                const uint64_t idx = (uint64_t)(f0 + f) * (uint64_t)Tn + (uint64_t)row0;
-                const u32x4 w0 = sr_words(seed, idx), w1 = sr_words(seed, idx + 8);
-                const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, b[4] = {w1.x, w1.y, w1.z, w1.w};
-                lo = e2m1_sr_pack8(z, a);
-                hi = e2m1_sr_pack8(z + 8, b);
-            } else {
-                lo = e2m1_rne_pack8(z);
-                hi = e2m1_rne_pack8(z + 8);
-            }
-            const uint32_t p = fg * 8 + (uint32_t)f;
-            *reinterpret_cast<uint2*>(&cols[col_slot<kTok>(p, ch)]) = make_uint2(lo, hi);
-            if ((ch & 1u) == 0) csc[p * kBlocks + ch / 2] = (uint8_t)(e8 + 127);
-        }
+        mx_tile_transposed<T, kSR>(tile, f0, row0, Tn, seed, fg, ch, cols, csc);
     }
     __syncthreads();
     write_staged_cols<kTok>(cols, codes, tf, tt, F, Tn);
     write_staged_scales<kThreads>(csc, kDualFeat, kBlocks, scales, Tn / 32, tf, F, tt / 32);
+}
+
+// Fused dual-orientation MXFP4 quantizer of the comparison format: one read of x [T x F] gives
+// the row-wise copy [T x F] (as mxfp4_quantize_1d makes it: 32-feature blocks, element index
+// row * F + col for SR) and the transposed copy [F x T] (as k_mx_quant_t makes it: 32-token
+// blocks, element index feature * T + token), on the staged quantizer's tiles.  A 32-feature
+// row block is the 8 features of four adjacent lanes (maximum by two DPP exchanges); a 32-token
+// block is the two chunks of lanes l and l + 32.  Both copies are staged in LDS and leave as
+// whole tile rows.  F % 32 == 0 and T % 32 == 0, so the lanes of a block are valid together.
+template <typename T, bool kSR>
+__global__ void __launch_bounds__(2 * dual_tile_tokens<kSR>(), dual_min_waves<T>())
+k_mx_quant_dual(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t seed,
+                uint64_t seed_t, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
+    constexpr int kTok = dual_tile_tokens<kSR>();
+    constexpr uint32_t kThreads = 2 * kTok, kBlocks = kTok / 32;
+    __shared__ uint32_t cols[kDualFeat * kTok / 8];
+    __shared__ uint8_t csc[kDualFeat * kBlocks];
+    __shared__ uint32_t rows[kTok * 32];
+    __shared__ uint8_t rsc[kTok * (kDualFeat / 32)];
+    uint32_t bx, by;
+    dual_tile((uint32_t)((F + kDualFeat - 1) / kDualFeat), bx, by);
+    const int64_t tf = (int64_t)bx * kDualFeat, tt = (int64_t)by * kTok;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t fg = lane & 31u, ch = 2u * (threadIdx.x >> 6) + (lane >> 5);
+    const int64_t f0 = tf + fg * 8, row0 = tt + ch * 16;
+    if (f0 < F && row0 < Tn) {
+        Tile16x8<T> tile;
+        tile.load(x + row0 * ld + f0, ld);
+        // row-wise: token row i, features f0 .. f0 + 7, one quarter of a 32-feature block
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float y[8];
+#pragma unroll
+            for (int f = 0; f < 8; ++f) y[f] = tile.get(i, f);
+            float m = 0.0f;
+#pragma unroll
+            for (int f = 0; f < 8; ++f) m = fmaxf(m, fabsf(y[f]));
+            m = fmaxf(m, swap_adjacent(m));
+            m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));
+            const int e8 = mx_exponent(m);
+            float z[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = __builtin_amdgcn_ldexpf(y[e], -e8);
+            uint32_t packed;
+            if constexpr (kSR) {
+                const u32x4 w = sr_words(seed, (uint64_t)(row0 + i) * (uint64_t)F + (uint64_t)f0);
+                const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+                packed = e2m1_sr_pack8(z, words);
+            } else {
+                packed = e2m1_rne_pack8(z);
+            }
+            const uint32_t r = ch * 16 + (uint32_t)i;
+            rows[row_slot(r) + fg] = packed;
+            if ((fg & 3u) == 0) rsc[r * (kDualFeat / 32) + fg / 4] = (uint8_t)(e8 + 127);
+        }
+        tile.fence();
+        mx_tile_transposed<T, kSR>(tile, f0, row0, Tn, seed_t, fg, ch, cols, csc);
+    }
+    __syncthreads();
+    write_staged_cols<kTok>(cols, codes_t, tf, tt, F, Tn);
+    write_staged_scales<kThreads>(csc, kDualFeat, kBlocks, scales_t, Tn / 32, tf, F, tt / 32);
+#pragma unroll 2
+    for (uint32_t j = threadIdx.x; j < kTok * 16; j += kThreads) {
+        const uint32_t r = j >> 4, q = j & 15u;
+        if (tt + r < Tn && tf + q * 16 < F)
+            *reinterpret_cast<uint2*>(codes + (tt + r) * (F / 2) + tf / 2 + q * 8) =
+                *reinterpret_cast<const uint2*>(&rows[row_slot(r) + 2 * q]);
+    }
+    write_staged_scales<kThreads>(rsc, kTok, kDualFeat / 32, scales, F / 32, tt, Tn, tf / 32);
 }
 
 static dim3 rht_grid(int64_t T, int64_t F) {
@@ -892,5 +989,38 @@ extern "C" nvfp4_status mxfp4_quantize_1d_t(const void* x, nvfp4_dtype dt, int64
         if (rnd == NVFP4_SR) NVFP4_MXT(float, true); else NVFP4_MXT(float, false);
     }
 #undef NVFP4_MXT
+    return launch_status();
+}
+
+extern "C" nvfp4_status mxfp4_quantize_dual(const void* x, nvfp4_dtype dt, int64_t ld,
+                                            nvfp4_round rnd, uint64_t seed, uint64_t seed_t,
+                                            const nvfp4_tensor* out, const nvfp4_tensor* out_t,
+                                            void* stream) {
+    nvfp4_status s = check_q(out, MXFP4_BLK_1x32, false);
+    if (s) return s;
+    s = check_q(out_t, MXFP4_BLK_1x32, false);
+    if (s) return s;
+    const int64_t T = out->rows, F = out->cols;
+    if (out_t->rows != F || out_t->cols != T) return NVFP4_ERR_SHAPE;
+    s = check_rht_input(x, dt, T, F, ld);
+    if (s) return s;
+    if (rnd != NVFP4_RNE && rnd != NVFP4_SR) return NVFP4_ERR_DTYPE;
+    if (T == 0 || F == 0) return NVFP4_OK;
+    hipStream_t st = as_stream(stream);
+#define NVFP4_MXD(TT, SRV)                                                                        \
+    do {                                                                                          \
+        const int64_t tiles = dual_grid(T, F, SRV);                                               \
+        if (tiles < 0) return NVFP4_ERR_SHAPE;                                                    \
+        hipLaunchKernelGGL((k_mx_quant_dual<TT, SRV>), dim3((uint32_t)tiles),                     \
+                           dim3(2 * dual_tile_tokens<SRV>()), 0, st, static_cast<const TT*>(x),   \
+                           T, F, ld, seed, seed_t, out->codes, out->scales, out_t->codes,         \
+                           out_t->scales);                                                        \
+    } while (0)
+    if (dt == NVFP4_BF16) {
+        if (rnd == NVFP4_SR) NVFP4_MXD(uint16_t, true); else NVFP4_MXD(uint16_t, false);
+    } else {
+        if (rnd == NVFP4_SR) NVFP4_MXD(float, true); else NVFP4_MXD(float, false);
+    }
+#undef NVFP4_MXD
     return launch_status();
 }

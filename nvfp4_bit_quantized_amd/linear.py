@@ -32,8 +32,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (RNE, SR, gemm, mx_gemm, mx_quantize_1d, mx_quantize_1d_t, quantize_1d, quantize_2d,
-               quantize_dual)
+from . import (RNE, SR, gemm, mx_gemm, mx_quantize_1d, mx_quantize_1d_t, mx_quantize_dual,
+               quantize_1d, quantize_2d, quantize_dual)
 
 _MASK64 = (1 << 64) - 1
 
@@ -80,15 +80,22 @@ class NVFP4LinearFn(torch.autograd.Function):
 class MXFP4LinearFn(torch.autograd.Function):
     """y = x W^T with every GEMM operand in MXFP4 and fp32 accumulation (the comparison format).
     forward   x, W -> MXFP4 row-wise (RNE); y = mx_gemm(x_q, W_q); when a gradient will be
-              needed, W^T [in x out] and x^T [in x T] are quantized (RNE) from one read each
-    backward  dY -> MXFP4 row-wise (SR, dgrad seed) and dY^T [out x T] (SR, wgrad seed);
-              dx = mx_gemm(dY_q, W^T_q), dW = mx_gemm(dY^T_q, x^T_q)."""
+              needed, the same read of x and of W also gives x^T [in x T] and W^T [in x out]
+              (mxfp4_quantize_dual)
+    backward  dY -> MXFP4 row-wise (SR, dgrad seed) and dY^T [out x T] (SR, wgrad seed), from one
+              read when both are needed; dx = mx_gemm(dY_q, W^T_q), dW = mx_gemm(dY^T_q, x^T_q)."""
 
     @staticmethod
     def forward(ctx, x: torch.Tensor, w: torch.Tensor, seed_dgrad: int, seed_wgrad: int):
         need_grad = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
-        y = mx_gemm(mx_quantize_1d(x, RNE), mx_quantize_1d(w, RNE), x.dtype)
-        ctx.q = (mx_quantize_1d_t(x, RNE), mx_quantize_1d_t(w, RNE)) if need_grad else None
+        if need_grad:
+            qx, qxt = mx_quantize_dual(x, RNE)
+            qw, qwt = mx_quantize_dual(w, RNE)
+            ctx.q = (qxt, qwt)
+        else:
+            qx, qw = mx_quantize_1d(x, RNE), mx_quantize_1d(w, RNE)
+            ctx.q = None
+        y = mx_gemm(qx, qw, x.dtype)
         ctx.seeds = (seed_dgrad, seed_wgrad)
         ctx.dtypes = (x.dtype, w.dtype)
         return y
@@ -100,9 +107,12 @@ class MXFP4LinearFn(torch.autograd.Function):
         x_dt, w_dt = ctx.dtypes
         dy = dy.contiguous()
         dx = dw = None
-        if ctx.needs_input_grad[0]:
+        if ctx.needs_input_grad[0] and ctx.needs_input_grad[1]:
+            qdy, qdyt = mx_quantize_dual(dy, SR, seed_dgrad, seed_wgrad)
+            dx, dw = mx_gemm(qdy, qwt, x_dt), mx_gemm(qdyt, qxt, w_dt)
+        elif ctx.needs_input_grad[0]:
             dx = mx_gemm(mx_quantize_1d(dy, SR, seed_dgrad), qwt, x_dt)
-        if ctx.needs_input_grad[1]:
+        elif ctx.needs_input_grad[1]:
             dw = mx_gemm(mx_quantize_1d_t(dy, SR, seed_wgrad), qxt, w_dt)
         ctx.q = None
         return dx, dw, None, None

@@ -163,6 +163,24 @@ def test_mx_transposed_validation(L):
     assert L.mxfp4_quantize_1d_t(FAKE, nv.BF16, 64, nv.RNE, 0, C.byref(nv_layout), None) == nv.ERR_LAYOUT
 
 
+def test_mx_dual_validation(L):
+    # x [T x F] = [96 x 64]: out [96 x 64], out_t [64 x 96]
+    q, qt = _q(96, 64, layout=nv.MX_1x32), _q(64, 96, layout=nv.MX_1x32)
+    f = L.mxfp4_quantize_dual
+    assert f(FAKE, nv.BF16, 64, 2, 0, 0, C.byref(q), C.byref(qt), None) == nv.ERR_DTYPE
+    assert f(FAKE, nv.BF16, 32, nv.RNE, 0, 0, C.byref(q), C.byref(qt), None) == nv.ERR_SHAPE
+    assert f(None, nv.BF16, 64, nv.RNE, 0, 0, C.byref(q), C.byref(qt), None) == nv.ERR_NULL
+    assert f(FAKE, nv.BF16, 64, nv.RNE, 0, 0, None, C.byref(qt), None) == nv.ERR_NULL
+    assert f(FAKE, nv.BF16, 64, nv.RNE, 0, 0, C.byref(q), None, None) == nv.ERR_NULL
+    wrong_t = _q(64, 64, layout=nv.MX_1x32)                  # not [F x T]
+    assert f(FAKE, nv.BF16, 64, nv.RNE, 0, 0, C.byref(q), C.byref(wrong_t), None) == nv.ERR_SHAPE
+    q48, qt48 = _q(48, 64, layout=nv.MX_1x32), _q(64, 48, layout=nv.MX_1x32)   # T % 32 != 0
+    assert f(FAKE, nv.BF16, 64, nv.RNE, 0, 0, C.byref(q48), C.byref(qt48), None) == nv.ERR_SHAPE
+    f48, ft48 = _q(96, 48, layout=nv.MX_1x32), _q(48, 96, layout=nv.MX_1x32)   # F % 32 != 0
+    assert f(FAKE, nv.BF16, 48, nv.RNE, 0, 0, C.byref(f48), C.byref(ft48), None) == nv.ERR_SHAPE
+    nv_layout = _q(96, 64)
+    assert f(FAKE, nv.BF16, 64, nv.RNE, 0, 0, C.byref(nv_layout), C.byref(qt), None) == nv.ERR_LAYOUT
+
 def test_dequantize_validation(L):
     q = _q(16, 32)
     assert L.nvfp4_dequantize(C.byref(q), None, nv.F32, 32, None) == nv.ERR_NULL
