@@ -144,10 +144,8 @@ __device__ __forceinline__ float hd16_absmax(float* v, const RhtPlan& p) {
     return m;
 }
 
-// In place: v <- (1/4) H16 v, butterflies in the order h = 1, 2, 4, 8 then one multiply by 1/4
-// each.  The random signs D are applied before, to the loaded tile (apply_signs), so that the
-// whole is (1/4) H16 D x with D applied first.
-__device__ __forceinline__ void h16_quarter(float* v) {
+// In place: v <- H16 v, butterflies in the order h = 1, 2, 4, 8.
+__device__ __forceinline__ void h16(float* v) {
 #pragma unroll
     for (int hs = 1; hs < 16; hs <<= 1)
 #pragma unroll
@@ -157,6 +155,13 @@ __device__ __forceinline__ void h16_quarter(float* v) {
                 v[i] = a + b;
                 v[i + hs] = a - b;
             }
+}
+
+// In place: v <- (1/4) H16 v, the butterflies then one multiply by 1/4 each.  The random signs D
+// are applied before, to the loaded tile (apply_signs), so that the whole is (1/4) H16 D x with D
+// applied first.
+__device__ __forceinline__ void h16_quarter(float* v) {
+    h16(v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = 0.25f * v[i];
 }
@@ -286,12 +291,22 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
 // The transposed copy of one thread's tile (features f0 .. f0 + 7 of the 16 tokens from row0):
 // for each feature f, the 16 tokens through (1/4) H16 D, one NVFP4 block of row f0 + f of the
 // [F x T] output, handed to emit(f, lo, hi, scale_byte) (codes of tokens 0-7 in lo, 8-15 in hi).
-template <typename T, bool kSR, bool kNoise, typename Emit>
+//
+// kFold (round to nearest only, and only while every nonzero encode factor stays >= 2^-124,
+// which a tensor amax A <= 2^120 ensures): the 1/4 goes into the block's encode factor instead
+// of into each element, z = v * fl(enc / 4) for v = H16 D x.  Where v / 4 and enc / 4 are normal
+// numbers both forms are the one rounding of v * enc / 4.  Where v / 4 is subnormal, z is below
+// 0.09 in both forms (a nonzero block scale needs amax_b * 448 / A >= 2^-10 with A >= 2^-100, and
+// enc <= 12 / amax_b), so both round to a zero code of v's sign.  The block maximum takes the 1/4
+// after the maximum (monotonic, so max fl(|v| / 4) = fl(max |v| / 4)).  One multiply per block
+// replaces one per element.
+template <typename T, bool kSR, bool kNoise, typename Emit, bool kFold = false>
 __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, int64_t f0,
                                                       int64_t row0, int64_t Tn, uint32_t mask,
                                                       const TensorScales& ts, const EncTable& tab,
                                                       uint64_t seed, double& g2, double& e2,
                                                       Emit emit) {
+    static_assert(!kFold || (!kSR && !kNoise), "the folded 1/4 is exact for round to nearest only");
     uint64_t idx = (uint64_t)f0 * (uint64_t)Tn + (uint64_t)row0;    // SR element index
     Tile16x8<T> sgn = tile;
     sgn.apply_signs(__builtin_amdgcn_readfirstlane(mask));     // the same in every lane
@@ -300,13 +315,15 @@ __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, i
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = sgn.get(i, f);
-        h16_quarter(v);
+        if constexpr (kFold) h16(v); else h16_quarter(v);
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        if constexpr (kFold) m = 0.25f * m;
         uint32_t sb;
         float enc;
         block_scale_tab(m, ts, tab, sb, enc);
+        if constexpr (kFold) enc = 0.25f * enc;
         float z[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) z[e] = v[e] * enc;
@@ -345,7 +362,8 @@ __device__ __forceinline__ void quant_tile_rows(const Tile16x8<T>& tile, int64_t
         float m = 0.0f;
 #pragma unroll
         for (int f = 0; f < 8; ++f) m = fmaxf(m, fabsf(y[f]));
-        m = fmaxf(m, swap_adjacent(m));
+        // m >= 0: the larger of two non-negative floats is the larger bit pattern
+        m = __uint_as_float(max(__float_as_uint(m), __float_as_uint(swap_adjacent(m))));
         uint32_t sb;
         float enc;
         block_scale_tab(m, ts, tab, sb, enc);
@@ -551,17 +569,22 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
                                     [&](int i, uint32_t packed, uint32_t sb) {
                                         const uint32_t r = ch * 16 + (uint32_t)i;
                                         stg.rows[row_slot(r) + fg] = packed;
-                                        if ((fg & 1u) == 0)
-                                            stg.rsc[r * 16 + (fg >> 1)] = (uint8_t)sb;
+                                        // both lanes of the pair store the same byte
+                                        stg.rsc[r * 16 + (fg >> 1)] = (uint8_t)sb;
                                     });
         double g2 = 0.0, e2 = 0.0;             // unused: no noise sums here
-        quant_tile_transposed<T, kSR, false>(
-            tile, f0, row0, Tn, rht_sign_mask(sign_seed), tst, tab_t, seed_t, g2, e2,
-            [&](int f, uint32_t lo, uint32_t hi, uint32_t sb) {
-                const uint32_t p = fg * 8 + (uint32_t)f;
-                *reinterpret_cast<uint2*>(&stg.cols[col_slot<kTok>(p, ch)]) = make_uint2(lo, hi);
-                stg.csc[p * kPieces + ch] = (uint8_t)sb;
-            });
+        auto to_stage = [&](int f, uint32_t lo, uint32_t hi, uint32_t sb) {
+            const uint32_t p = fg * 8 + (uint32_t)f;
+            *reinterpret_cast<uint2*>(&stg.cols[col_slot<kTok>(p, ch)]) = make_uint2(lo, hi);
+            stg.csc[p * kPieces + ch] = (uint8_t)sb;
+        };
+        const uint32_t mask = rht_sign_mask(sign_seed);
+        if (!kSR && At <= 0x1p120f)            // the same branch in every lane
+            quant_tile_transposed<T, kSR, false, decltype(to_stage), !kSR>(
+                tile, f0, row0, Tn, mask, tst, tab_t, seed_t, g2, e2, to_stage);
+        else
+            quant_tile_transposed<T, kSR, false>(tile, f0, row0, Tn, mask, tst, tab_t, seed_t, g2,
+                                                 e2, to_stage);
     }
     __syncthreads();
     write_staged_cols<kTok>(stg.cols, codes_t, tf, tt, F, Tn);
