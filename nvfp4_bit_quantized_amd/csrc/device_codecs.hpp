@@ -170,6 +170,24 @@ __device__ __forceinline__ u32x4 sr_words(uint64_t seed, uint64_t idx8) {
 }
 
 // ---- loads ----------------------------------------------------------------------------------
+// 16-byte load.  kNT: with the nontemporal hint, for an input read for the last time -- the
+// lines are not kept in the caches for later readers (measured on 16384 x 20480 bf16 tensors:
+// the dual quantizers 6-8% faster).  A pass whose input is read again next (an amax pass ahead of
+// its quantizer) loads normally when the tensor fits the 256 MB last-level cache.
+template <bool kNT>
+__device__ __forceinline__ uint4 load16(const void* p) {
+    if constexpr (kNT) {
+        typedef unsigned int u32v4 __attribute__((ext_vector_type(4)));
+        const u32v4 v = __builtin_nontemporal_load(reinterpret_cast<const u32v4*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+}
+
+// Tensors of at least this many bytes do not fit the last-level cache: their amax pass streams.
+constexpr int64_t kStreamBytes = 256ll << 20;
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

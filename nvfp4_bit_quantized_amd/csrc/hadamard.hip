@@ -33,9 +33,10 @@ template <typename T> struct Tile16x8;
 
 template <> struct Tile16x8<uint16_t> {
     uint4 w[16];
+    template <bool kNT = true>
     __device__ __forceinline__ void load(const uint16_t* p, int64_t ld) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) w[i] = *reinterpret_cast<const uint4*>(p + i * ld);
+        for (int i = 0; i < 16; ++i) w[i] = load16<kNT>(p + i * ld);
     }
     __device__ __forceinline__ float get(int i, int f) const {
         const uint32_t v = f < 2 ? w[i].x : f < 4 ? w[i].y : f < 6 ? w[i].z : w[i].w;
@@ -61,11 +62,15 @@ template <> struct Tile16x8<uint16_t> {
 
 template <> struct Tile16x8<float> {
     float4 a[16], b[16];
+    template <bool kNT = true>
     __device__ __forceinline__ void load(const float* p, int64_t ld) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            a[i] = reinterpret_cast<const float4*>(p + i * ld)[0];
-            b[i] = reinterpret_cast<const float4*>(p + i * ld)[1];
+            const uint4 u = load16<kNT>(p + i * ld), v = load16<kNT>(p + i * ld + 4);
+            a[i] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                               __uint_as_float(u.w));
+            b[i] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                               __uint_as_float(v.w));
         }
     }
     __device__ __forceinline__ float get(int i, int f) const {
@@ -219,7 +224,7 @@ __device__ __forceinline__ void rht_amax_tile(const Tile16x8<T>& t16, const RhtP
     }
 }
 
-template <typename T, bool kPlain, int kRhtAmaxSub = rht_amax_sub<T>()>
+template <typename T, bool kPlain, bool kNT, int kRhtAmaxSub = rht_amax_sub<T>()>
 __global__ void __launch_bounds__(kRhtThreads * kRhtAmaxSub)
 k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t sign_seed,
            float* amax_out, float* amax_plain_out, uint32_t tiles, FastDiv tiles_per_row) {
@@ -243,13 +248,13 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
         // two register sets with fixed roles; a clamped tile past the end is a harmless duplicate
         Tile16x8<T> ta, tb;
         float mb = 0.0f, mpb = 0.0f;
-        ta.load(tile_ptr(tile), ld);
+        ta.template load<kNT>(tile_ptr(tile), ld);
         for (; tile < tiles; tile += 2 * stride) {
-            tb.load(tile_ptr(tile + stride), ld);
+            tb.template load<kNT>(tile_ptr(tile + stride), ld);
             __builtin_amdgcn_sched_barrier(0);
             rht_amax_tile<T, kPlain>(ta, plan, m, mp);
             __builtin_amdgcn_sched_barrier(0);
-            ta.load(tile_ptr(tile + 2 * stride), ld);
+            ta.template load<kNT>(tile_ptr(tile + 2 * stride), ld);
             __builtin_amdgcn_sched_barrier(0);
             rht_amax_tile<T, kPlain>(tb, plan, mb, mpb);
             __builtin_amdgcn_sched_barrier(0);
@@ -259,7 +264,7 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
     } else {
         for (; tile < tiles; tile += stride) {
             Tile16x8<T> cur;
-            cur.load(tile_ptr(tile), ld);
+            cur.template load<kNT>(tile_ptr(tile), ld);
             rht_amax_tile<T, kPlain>(cur, plan, m, mp);
         }
     }
@@ -579,8 +584,10 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
             stg.csc[p * kPieces + ch] = (uint8_t)sb;
         };
         const uint32_t mask = rht_sign_mask(sign_seed);
-        if (!kSR && At <= 0x1p120f)            // the same branch in every lane
-            quant_tile_transposed<T, kSR, false, decltype(to_stage), !kSR>(
+        // the fold for bf16 input (the fp32 tile leaves no registers for a second code path)
+        constexpr bool kFoldable = !kSR && sizeof(T) == 2;
+        if (kFoldable && At <= 0x1p120f)       // the same branch in every lane
+            quant_tile_transposed<T, kSR, false, decltype(to_stage), kFoldable>(
                 tile, f0, row0, Tn, mask, tst, tab_t, seed_t, g2, e2, to_stage);
         else
             quant_tile_transposed<T, kSR, false>(tile, f0, row0, Tn, mask, tst, tab_t, seed_t, g2,
@@ -803,14 +810,18 @@ static nvfp4_status launch_rht_amax(const void* x, nvfp4_dtype dt, int64_t T, in
         const uint32_t need = (tiles + sub - 1) / sub;
         const dim3 grid(need < (uint32_t)kRhtAmaxBlocks ? need : (uint32_t)kRhtAmaxBlocks);
         const dim3 block(kRhtThreads * sub);
-#define NVFP4_RA(TT, PLAIN)                                                                       \
-        hipLaunchKernelGGL((k_rht_amax<TT, PLAIN>), grid, block, 0, st, static_cast<const TT*>(x), \
-                           T, F, ld, sign_seed, dst, plain_dst, tiles, tpr)
+        const bool stream = T * F * (dt == NVFP4_BF16 ? 2 : 4) >= kStreamBytes;
+#define NVFP4_RA(TT, PLAIN, NT)                                                                   \
+        hipLaunchKernelGGL((k_rht_amax<TT, PLAIN, NT>), grid, block, 0, st,                       \
+                           static_cast<const TT*>(x), T, F, ld, sign_seed, dst, plain_dst, tiles, tpr)
+#define NVFP4_RA2(TT, PLAIN)                                                                      \
+        do { if (stream) NVFP4_RA(TT, PLAIN, true); else NVFP4_RA(TT, PLAIN, false); } while (0)
         if (dt == NVFP4_BF16) {
-            if (plain_dst) NVFP4_RA(uint16_t, true); else NVFP4_RA(uint16_t, false);
+            if (plain_dst) NVFP4_RA2(uint16_t, true); else NVFP4_RA2(uint16_t, false);
         } else {
-            if (plain_dst) NVFP4_RA(float, true); else NVFP4_RA(float, false);
+            if (plain_dst) NVFP4_RA2(float, true); else NVFP4_RA2(float, false);
         }
+#undef NVFP4_RA2
 #undef NVFP4_RA
     }
     return launch_status();

@@ -25,19 +25,22 @@ constexpr int kNoiseBlocks = 1024;   // grid cap of the quantizer with the noise
 template <typename T> struct Group8;
 
 template <> struct Group8<uint16_t> {   // bf16
+    template <bool kNT = true>
     static __device__ __forceinline__ void load(const uint16_t* p, float* y) {
-        uint4 v = *reinterpret_cast<const uint4*>(p);
+        const uint4 v = load16<kNT>(p);
         y[0] = bf16_lo(v.x); y[1] = bf16_hi(v.x); y[2] = bf16_lo(v.y); y[3] = bf16_hi(v.y);
         y[4] = bf16_lo(v.z); y[5] = bf16_hi(v.z); y[6] = bf16_lo(v.w); y[7] = bf16_hi(v.w);
     }
 };
 
 template <> struct Group8<float> {
+    template <bool kNT = true>
     static __device__ __forceinline__ void load(const float* p, float* y) {
-        float4 a = reinterpret_cast<const float4*>(p)[0];
-        float4 b = reinterpret_cast<const float4*>(p)[1];
-        y[0] = a.x; y[1] = a.y; y[2] = a.z; y[3] = a.w;
-        y[4] = b.x; y[5] = b.y; y[6] = b.z; y[7] = b.w;
+        const uint4 a = load16<kNT>(p), b = load16<kNT>(p + 4);
+        y[0] = __uint_as_float(a.x); y[1] = __uint_as_float(a.y);
+        y[2] = __uint_as_float(a.z); y[3] = __uint_as_float(a.w);
+        y[4] = __uint_as_float(b.x); y[5] = __uint_as_float(b.y);
+        y[6] = __uint_as_float(b.z); y[7] = __uint_as_float(b.w);
     }
 };
 
@@ -66,7 +69,7 @@ constexpr int kAmaxBlocks = 256;
 constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxUnroll = 8;
 
-template <typename T>
+template <typename T, bool kNT>
 __global__ void __launch_bounds__(kAmaxThreads)
 k_amax(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, float* amax_out) {
     float m = 0.0f;
@@ -80,7 +83,7 @@ k_amax(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, float*
             g = g < groups ? g : groups - 1;           // clamped duplicate: max is unchanged
             const uint32_t row = fastdiv(g, gpr);
             const uint32_t cg = g - row * gpr.d;
-            Group8<T>::load(x + (int64_t)row * ld + cg * 8, y[u]);
+            Group8<T>::template load<kNT>(x + (int64_t)row * ld + cg * 8, y[u]);
         }
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; ++u)
@@ -529,12 +532,16 @@ static nvfp4_status launch_amax(const void* x, nvfp4_dtype dt, int64_t rows, int
         const uint32_t groups = (uint32_t)g64;
         const FastDiv gpr = make_fastdiv((uint32_t)(cols / 8));
         const dim3 grid(amax_grid(groups));
-        if (dt == NVFP4_BF16)
-            hipLaunchKernelGGL(k_amax<uint16_t>, grid, dim3(kAmaxThreads), 0, st,
-                               static_cast<const uint16_t*>(x), ld, groups, gpr, dst);
-        else
-            hipLaunchKernelGGL(k_amax<float>, grid, dim3(kAmaxThreads), 0, st,
-                               static_cast<const float*>(x), ld, groups, gpr, dst);
+        const bool stream = rows * cols * (dt == NVFP4_BF16 ? 2 : 4) >= kStreamBytes;
+#define NVFP4_AMAX(TT, NT)                                                                        \
+    hipLaunchKernelGGL((k_amax<TT, NT>), grid, dim3(kAmaxThreads), 0, st,                         \
+                       static_cast<const TT*>(x), ld, groups, gpr, dst)
+        if (dt == NVFP4_BF16) {
+            if (stream) NVFP4_AMAX(uint16_t, true); else NVFP4_AMAX(uint16_t, false);
+        } else {
+            if (stream) NVFP4_AMAX(float, true); else NVFP4_AMAX(float, false);
+        }
+#undef NVFP4_AMAX
     }
     return launch_status();
 }
