@@ -190,6 +190,16 @@ NVFP4_API nvfp4_status nvfp4_hadamard_quantize_noise(const void *x, nvfp4_dtype 
 NVFP4_API nvfp4_status nvfp4_dual_amax(const void *x, nvfp4_dtype dt, int64_t T, int64_t F, int64_t ld,
                                        uint64_t sign_seed, float *amax_out, float *amax_t_out, void *stream);
 
+/* Accumulating form of nvfp4_dual_amax [P3 Come funziona NVFP4?: the per-tensor level of the
+ * scaling]: *amax_inout = max(*amax_inout, max |x|) and *amax_t_inout = max(*amax_t_inout,
+ * max |(1/4) H16 D x|), with no zero-fill first, as nvfp4_amax_accumulate: the caller initialises
+ * both (0 gives the amaxes of x alone), so that one operation can clear every amax slot of a
+ * training step.  Both must hold non-negative, non-NaN floats and be distinct; an empty x leaves
+ * them unchanged.  Shape rules and errors as nvfp4_dual_amax. */
+NVFP4_API nvfp4_status nvfp4_dual_amax_accumulate(const void *x, nvfp4_dtype dt, int64_t T, int64_t F,
+                                                  int64_t ld, uint64_t sign_seed, float *amax_inout,
+                                                  float *amax_t_inout, void *stream);
+
 /* Fused dual-orientation quantization: one read of an activation or gradient x [T tokens x
  * F features] (row stride ld) writes both NVFP4 copies a training step takes from it
  * [P2 Describir: all three GEMMs on FP4 operands; P1 Metodologia: random Hadamard transforms on

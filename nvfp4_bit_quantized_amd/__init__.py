@@ -26,7 +26,7 @@ SYMBOLS = ("nvfp4_status_string", "nvfp4_amax", "nvfp4_hadamard_amax", "nvfp4_qu
            "nvfp4_quantize_1d_noise", "nvfp4_qdq", "mxfp4_quantize_1d_t", "nvfp4_amax_accumulate",
            "nvfp4_hadamard_amax_accumulate", "nvfp4_hadamard_quantize_noise", "nvfp4_gemm_ws",
            "nvfp4_gemm_workspace_size", "nvfp4_gemm_ws_noalloc", "mxfp4_gemm_ws",
-           "mxfp4_gemm_workspace_size", "mxfp4_quantize_dual")
+           "mxfp4_gemm_workspace_size", "mxfp4_quantize_dual", "nvfp4_dual_amax_accumulate")
 
 
 class NvTensor(C.Structure):
@@ -70,6 +70,7 @@ def lib():
         L.mxfp4_quantize_1d_t.argtypes = [P, i32, i64, i32, u64, T, P]
         L.mxfp4_quantize_dual.argtypes = [P, i32, i64, i32, u64, u64, T, T, P]
         L.nvfp4_dual_amax.argtypes = [P, i32, i64, i64, i64, u64, P, P, P]
+        L.nvfp4_dual_amax_accumulate.argtypes = [P, i32, i64, i64, i64, u64, P, P, P]
         L.nvfp4_quantize_dual.argtypes = [P, i32, i64, u64, P, P, i32, u64, u64, T, T, P]
         L.nvfp4_quantize_1d_noise.argtypes = [P, i32, i64, P, i32, u64, T, P, P]
         L.nvfp4_qdq.argtypes = [P, i32, i64, i64, i64, i32, i32, P, i32, u64, P, i64, P, P, P]
@@ -280,6 +281,16 @@ def dual_amax(x: torch.Tensor, sign_seed: int, out: torch.Tensor | None = None,
                                                     sign_seed, _ptr(out), _ptr(out_t),
                                                     _stream(x.device)))
     return out, out_t
+
+
+def dual_amax_accumulate(x: torch.Tensor, sign_seed: int, acc: torch.Tensor, acc_t: torch.Tensor):
+    """acc <- max(acc, amax of x), acc_t <- max(acc_t, amax of its random Hadamard transform),
+    from one read of x [T x F]; both caller-initialised (>= 0), no zero-fill."""
+    x, dt, ld = _x(x)
+    _check("nvfp4_dual_amax_accumulate",
+           lib().nvfp4_dual_amax_accumulate(_ptr(x), dt, x.shape[0], x.shape[1], ld, sign_seed,
+                                            _ptr(acc), _ptr(acc_t), _stream(x.device)))
+    return acc, acc_t
 
 
 def quantize_dual(x: torch.Tensor, sign_seed: int, rounding: int = RNE, seed: int = 0,

@@ -867,6 +867,18 @@ extern "C" nvfp4_status nvfp4_dual_amax(const void* x, nvfp4_dtype dt, int64_t T
     return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_t_out, amax_out, as_stream(stream));
 }
 
+extern "C" nvfp4_status nvfp4_dual_amax_accumulate(const void* x, nvfp4_dtype dt, int64_t T,
+                                                   int64_t F, int64_t ld, uint64_t sign_seed,
+                                                   float* amax_inout, float* amax_t_inout,
+                                                   void* stream) {
+    nvfp4_status s = check_rht_input(x, dt, T, F, ld);
+    if (s) return s;
+    if ((s = check_amax_ptr(amax_inout)) || (s = check_amax_ptr(amax_t_inout))) return s;
+    if (amax_inout == amax_t_inout) return NVFP4_ERR_SHAPE;
+    return launch_rht_amax(x, dt, T, F, ld, sign_seed, amax_t_inout, amax_inout, as_stream(stream),
+                           true);
+}
+
 constexpr uint32_t kNoiseWorkgroups = 1024;   // target grid size of the quantizer with noise sums
 
 static nvfp4_status hadamard_quantize(const void* x, nvfp4_dtype dt, int64_t ld, uint64_t sign_seed,

@@ -181,6 +181,16 @@ def test_mx_dual_validation(L):
     nv_layout = _q(96, 64)
     assert f(FAKE, nv.BF16, 64, nv.RNE, 0, 0, C.byref(nv_layout), C.byref(qt), None) == nv.ERR_LAYOUT
 
+def test_dual_amax_accumulate_validation(L):
+    f = L.nvfp4_dual_amax_accumulate
+    assert f(FAKE, nv.BF16, 24, 64, 64, 0, FAKE, FAKE + 4, None) == nv.ERR_SHAPE       # T % 16
+    assert f(FAKE, nv.BF16, 32, 60, 64, 0, FAKE, FAKE + 4, None) == nv.ERR_SHAPE       # F % 8
+    assert f(FAKE, nv.BF16, 32, 64, 64, 0, None, FAKE + 4, None) == nv.ERR_NULL
+    assert f(FAKE, nv.BF16, 32, 64, 64, 0, FAKE, None, None) == nv.ERR_NULL
+    assert f(FAKE, nv.BF16, 32, 64, 64, 0, FAKE + 2, FAKE + 4, None) == nv.ERR_ALIGN
+    assert f(FAKE, nv.BF16, 32, 64, 64, 0, FAKE, FAKE, None) == nv.ERR_SHAPE           # same slot
+    assert f(None, nv.BF16, 32, 64, 64, 0, FAKE, FAKE + 4, None) == nv.ERR_NULL
+
 def test_dequantize_validation(L):
     q = _q(16, 32)
     assert L.nvfp4_dequantize(C.byref(q), None, nv.F32, 32, None) == nv.ERR_NULL
