@@ -1,7 +1,10 @@
 """GPU parity at the edges of the formats' ranges (the degenerate cases of the method), fp32
 inputs from workloads.edge_fp32: fp32 subnormals with the tensor amax below the 2^-100 zero
 threshold, an amax just above it, an amax near the top of the fp32 range, blocks whose E4M3 scale
-is subnormal or zero next to large blocks, and signed zeros.  Every quantizer's codes, scale
+is subnormal or zero next to large blocks, signed zeros, subnormal values beside normal ones, and
+Hadamard-transformed amaxes just below and above 2^120; the same tensors in bf16 through the
+Hadamard, dual and MXFP4 dual quantizers (whose bf16 round-to-nearest path folds the transform's
+1/4 into the encode factor while the amax is at most 2^120).  Every quantizer's codes, scale
 bytes, amax and s_dec must equal the oracle's bit for bit; dequantized values exactly; a GEMM of
 each tensor with a normal weight within relative L2 1e-5."""
 import numpy as np
@@ -14,7 +17,7 @@ from gemm_check import assert_gemm_close
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-KINDS = ["tiny", "near_zero", "huge", "wide", "signed_zeros"]
+KINDS = ["tiny", "near_zero", "huge", "wide", "signed_zeros", "tiny_mix", "below_2p120", "above_2p120"]
 SIGN = 0x51E40006
 
 
@@ -102,3 +105,26 @@ def test_edge_gemm(nv, orc, kind):
         assert not got.any()
     else:
         assert_gemm_close(got, ref, "edge gemm")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_edge_bf16_hadamard_and_dual(nv, orc, kind, rounding):
+    x = W.edge_fp32(kind, (64, 48), 47, torch.bfloat16)
+    xb = W.bits(x)
+    g = nv.hadamard_quantize(x.to(DEV), SIGN, rounding, seed=12)
+    _same_q(g, orc.hadamard_quantize(xb, SIGN, rounding, 12), f"bf16 rht {kind}")
+    q, qt = nv.quantize_dual(x.to(DEV), SIGN, rounding, seed=13, seed_t=14)
+    _same_q(q, orc.quantize_1d(xb, rounding, 13), f"bf16 dual rows {kind}")
+    _same_q(qt, orc.hadamard_quantize(xb, SIGN, rounding, 14), f"bf16 dual transposed {kind}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_edge_bf16_mx_dual(nv, orc, kind, rounding):
+    x = W.edge_fp32(kind, (64, 64), 48, torch.bfloat16)
+    xb = W.bits(x)
+    q, qt = nv.mx_quantize_dual(x.to(DEV), rounding, seed=15, seed_t=16)
+    _same_q(q, orc.mx_quantize_1d(xb, rounding, 15), f"bf16 mx dual rows {kind}", scalars=False)
+    _same_q(qt, orc.mx_quantize_1d(np.ascontiguousarray(xb.T), rounding, 16),
+            f"bf16 mx dual transposed {kind}", scalars=False)

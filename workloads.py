@@ -43,16 +43,31 @@ def normal(shape, sigma: float, seed: int, spike_frac: float = 0.0, spike_mult: 
     return _finish(v, shape, dtype)
 
 
-def edge_fp32(kind: str, shape, seed: int) -> torch.Tensor:
-    """fp32 tensors at the edges of the formats' ranges (the degenerate cases of the method):
+def edge_fp32(kind: str, shape, seed: int, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Tensors at the edges of the formats' ranges (the degenerate cases of the method), fp32
+    unless dtype says otherwise (bf16 has the same exponent range):
       "tiny"       N(0,1) * 1e-38: fp32 subnormals, amax below the 2^-100 zero threshold
       "near_zero"  N(0,1) * 1e-29: amax just above that threshold (huge tensor scale factors)
       "huge"       N(0,1) * 1e37: amax near the top of the fp32 range
       "wide"       random signs times 2^u, u uniform in [-70, 12): blocks whose E4M3 scale is
                    subnormal or zero next to blocks with large values
-      "signed_zeros" mostly +0 and -0, with 1% N(0,1) entries."""
+      "signed_zeros" mostly +0 and -0, with 1% N(0,1) entries
+      "tiny_mix"   N(0,1) * 2^-131 (subnormal) with 2% of the entries times 2^36: an amax
+                   around 2^-93, blocks of subnormal values, and subnormal values beside
+                   normal ones in a block
+      "below_2p120", "above_2p120"  N(0,1) * 2^115 and * 2^119: a Hadamard-transformed amax just
+                   below and just above 2^120."""
     rng = _rng(seed)
     n = int(np.prod(shape))
+    if kind == "tiny_mix":
+        v = rng.standard_normal(n) * 2.0 ** -131
+        k = n // 50
+        idx = rng.choice(n, k, replace=False)
+        v[idx] = v[idx] * 2.0 ** 36
+        return _finish(v, shape, dtype)
+    if kind in ("below_2p120", "above_2p120"):
+        v = rng.standard_normal(n) * 2.0 ** (115 if kind == "below_2p120" else 119)
+        return _finish(v, shape, dtype)
     if kind == "tiny":
         v = rng.standard_normal(n) * 1e-38
     elif kind == "near_zero":
@@ -68,7 +83,7 @@ def edge_fp32(kind: str, shape, seed: int) -> torch.Tensor:
             v[rng.choice(n, k, replace=False)] = rng.standard_normal(k)
     else:
         raise ValueError(kind)
-    return _finish(v, shape, torch.float32)
+    return _finish(v, shape, dtype)
 
 
 def student_t(shape, nu: float, seed: int, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
