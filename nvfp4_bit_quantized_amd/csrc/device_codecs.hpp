@@ -103,7 +103,10 @@ __device__ __forceinline__ void block_scale_tab(float amax_b, const TensorScales
 // sign kept), packed element 2j -> low nibble of byte j.  gfx950's v_cvt_scalef32_pk_fp4_f32
 // with a unit scale performs exactly this rounding for every finite fp32 input.
 __device__ __forceinline__ uint32_t e2m1_rne_pack8(const float* z) {
+    // each conversion writes one byte of w and keeps the other three, so the four together
+    // overwrite all of it: w's starting value is never seen (no instruction to set it)
     uint32_t w = 0;
+    w = __builtin_nondeterministic_value(w);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[0], z[1], 1.0f, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[2], z[3], 1.0f, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[4], z[5], 1.0f, 2);
