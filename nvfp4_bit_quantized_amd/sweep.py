@@ -8,13 +8,17 @@ quantization MSE ||Q(x) - x||^2 / ||x||^2 (summed in the same pass), and, per GE
 L2 error of the product of the dequantized operands against the product of the originals.  The
 products themselves are an analysis step, not part of the training path: they run as fp32
 matrix products (torch, full fp32 precision) on the dequantized values, whose accumulation error
-(~1e-6) is far below the quantization errors measured (~1e-2 to 1e-1).
+(~1e-6) is far below the quantization errors measured (~1e-2 to 1e-1).  The two configurations
+the library trains with, NVFP4 (block 16, E4M3) and MXFP4 (block 32, E8M0), also get the error of
+the training path itself (``gemm_library``): the operands through the library's 1D quantizers
+(the same codes as the sweep kernel's, with the same seeds) and the product through its NVFP4 or
+MXFP4 GEMM.
 """
 from __future__ import annotations
 
 import torch
 
-from . import E4M3, E8M0, RNE, SR, qdq
+from . import E4M3, E8M0, RNE, SR, gemm, mx_gemm, mx_quantize_1d, qdq, quantize_1d
 
 CONFIGS = [(b, f, r) for b in (8, 16, 32) for f in (E4M3, E8M0) for r in (RNE, SR)]
 
@@ -45,12 +49,27 @@ def gemm_rel_error(a: torch.Tensor, b: torch.Tensor, block: int, fmt: int, round
     return float(torch.linalg.norm(qa @ qb.t() - ref) / torch.linalg.norm(ref))
 
 
+def gemm_library_rel_error(a: torch.Tensor, b: torch.Tensor, block: int, fmt: int, rounding_a: int,
+                           rounding_b: int, seed: int, ref: torch.Tensor) -> float | None:
+    """The same error through the training path: NVFP4 (block 16, E4M3) or MXFP4 (block 32, E8M0)
+    operands from the library's 1D quantizers (seeds as in gemm_rel_error) multiplied by its
+    GEMM with fp32 output; None for the configurations the library does not train with."""
+    if (block, fmt) == (16, E4M3):
+        c = gemm(quantize_1d(a, rounding_a, seed), quantize_1d(b, rounding_b, seed + 1))
+    elif (block, fmt) == (32, E8M0):
+        c = mx_gemm(mx_quantize_1d(a, rounding_a, seed), mx_quantize_1d(b, rounding_b, seed + 1))
+    else:
+        return None
+    return float(torch.linalg.norm(c - ref) / torch.linalg.norm(ref))
+
+
 def format_sweep(tensors: dict, gemms: list, configs=CONFIGS) -> dict:
     """tensors: name -> 2-D tensor (K contiguous).  gemms: (name, A, B, a_is_gradient) with
     C = A B^T.  Following the recipe (forward operands round to nearest, gradients
     stochastically), a gradient A takes the configuration's rounding and every other operand
     rounds to nearest; the per-tensor MSE uses the configuration's rounding for every tensor.
-    Returns {config: {"bits": b, "mse": {tensor: rel MSE}, "gemm": {gemm: rel L2}}}."""
+    Returns {config: {"bits": b, "mse": {tensor: rel MSE}, "gemm": {gemm: rel L2}}}, with
+    "gemm_library" ({gemm: rel L2} through the library's quantizers and GEMMs) for NVFP4 and MXFP4."""
     prev = torch.backends.cuda.matmul.allow_tf32
     torch.backends.cuda.matmul.allow_tf32 = False
     try:
@@ -64,6 +83,9 @@ def format_sweep(tensors: dict, gemms: list, configs=CONFIGS) -> dict:
             for name, a, b, a_grad in gemms:
                 ra = rnd if a_grad else RNE
                 res["gemm"][name] = gemm_rel_error(a, b, block, fmt, ra, RNE, 11, refs[name])
+                lib_err = gemm_library_rel_error(a, b, block, fmt, ra, RNE, 11, refs[name])
+                if lib_err is not None:
+                    res.setdefault("gemm_library", {})[name] = lib_err
             out[config_name(block, fmt, rnd)] = res
         return out
     finally:
@@ -71,4 +93,4 @@ def format_sweep(tensors: dict, gemms: list, configs=CONFIGS) -> dict:
 
 
 __all__ = ["CONFIGS", "config_name", "bits_per_element", "rel_mse", "gemm_rel_error",
-           "format_sweep"]
+           "gemm_library_rel_error", "format_sweep"]
