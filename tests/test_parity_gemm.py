@@ -49,6 +49,18 @@ def _check_gemm(nv, orc, qa, qb, rows=None, mx=False, bf16_too=True):
         torch.cuda.synchronize()
         exp = c.cpu().to(torch.bfloat16)
         assert torch.equal(cb.cpu().view(torch.int16), exp.view(torch.int16))
+        # and against the oracle itself: the float64 result rounded to bf16, equal except where
+        # the fp32 accumulation lands on the other side of a bf16 rounding point (then one ulp)
+        gb = cb.cpu() if rows is None else cb.cpu()[torch.as_tensor(rows)]
+        rb = torch.from_numpy(np.ascontiguousarray(ref)).to(torch.float32).to(torch.bfloat16)
+        gi = gb.view(torch.int16).to(torch.int32)
+        ri = rb.view(torch.int16).to(torch.int32)
+        equal = gb.float() == rb.float()                  # +0 and -0 count as equal
+        same_sign = (gb.float() * rb.float() > 0) | equal
+        assert bool(same_sign.all()), "bf16 output: a sign differs from the oracle's"
+        ulps = torch.where(equal, torch.zeros_like(gi), (gi - ri).abs())
+        assert int(ulps.max()) <= 1, f"bf16 output: {int(ulps.max())} ulps from the oracle's"
+        assert float((ulps == 0).float().mean()) >= 0.999, "bf16 output: too many one-ulp differences"
     return err
 
 
