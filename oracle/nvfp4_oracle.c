@@ -17,10 +17,11 @@
  *        prestazioni a 4 bit" (massacarraranews.com)
  * Where the pages are silent the reading taken is named in the comment ("reading: ...").
  *
- * Parity unpinned (no page value or closed form fixes them; the GPU only has to agree):
+ * Pinned within rounding rather than bit for bit (the orders are readings; their results equal
+ * the exact-arithmetic definitions except within a few fp32 roundings of a rounding midpoint):
  *   - the fp32 operation order of the block scale step (t = amax_b * k1, enc = s_enc / scale);
  *     the tensor scales themselves ARE pinned as single correctly rounded divisions;
- *   - the butterfly order of the 16-point Hadamard transform (its matrix IS pinned).
+ *   - the butterfly order of the 16-point Hadamard transform (its matrix IS pinned exactly).
  * The Philox generator is pinned by its published known answers, and the two maps that draw
  * from it are pinned by the properties a random draw must have (balanced, pairwise independent
  * Hadamard signs; an injective, pairwise independent element -> SR draw map).  WHICH output
