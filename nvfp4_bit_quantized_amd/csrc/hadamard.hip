@@ -297,21 +297,28 @@ k_rht_amax(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_t 
 // for each feature f, the 16 tokens through (1/4) H16 D, one NVFP4 block of row f0 + f of the
 // [F x T] output, handed to emit(f, lo, hi, scale_byte) (codes of tokens 0-7 in lo, 8-15 in hi).
 //
-// kFold (round to nearest only, and only while every nonzero encode factor stays >= 2^-124,
-// which a tensor amax A <= 2^120 ensures): the 1/4 goes into the block's encode factor instead
-// of into each element, z = v * fl(enc / 4) for v = H16 D x.  Where v / 4 and enc / 4 are normal
-// numbers both forms are the one rounding of v * enc / 4.  Where v / 4 is subnormal, z is below
-// 0.09 in both forms (a nonzero block scale needs amax_b * 448 / A >= 2^-10 with A >= 2^-100, and
-// enc <= 12 / amax_b), so both round to a zero code of v's sign.  The block maximum takes the 1/4
-// after the maximum (monotonic, so max fl(|v| / 4) = fl(max |v| / 4)).  One multiply per block
-// replaces one per element.
+// kFold (only while every nonzero encode factor stays >= 2^-124, which a tensor amax A <= 2^120
+// ensures): the 1/4 goes into the block's encode factor instead of into each element,
+// z = v * fl(enc / 4) for v = H16 D x.  Where v / 4 and enc / 4 are both exact, the two forms
+// are the one rounding of v * enc / 4, so z is the same number bit for bit and any rounding
+// of it, nearest or stochastic, gives the same code.  enc / 4 is exact above 2^-124.  v / 4 is
+// exact for bf16 input: every bf16 value is a multiple of 2^-133 (its smallest subnormal), so
+// every butterfly sum is too (below 2^-110 it needs at most 23 bits and is not rounded, above
+// it the fp32 spacing is itself a multiple of 2^-133), and v / 4, a multiple of 2^-135, is an
+// fp32 number.  For fp32 input v / 4 can round where it is subnormal; then z is below 0.09 in
+// both forms (a nonzero block scale needs amax_b * 448 / A >= 2^-10 with A >= 2^-100, and
+// enc <= 12 / amax_b), which round to nearest sends to a zero code of v's sign either way, but
+// a stochastic rounding of the two could differ.  The block maximum takes the 1/4 after the
+// maximum (monotonic, so max fl(|v| / 4) = fl(max |v| / 4)).  One multiply per block replaces
+// one per element.
 template <typename T, bool kSR, bool kNoise, typename Emit, bool kFold = false>
 __device__ __forceinline__ void quant_tile_transposed(const Tile16x8<T>& tile, int64_t f0,
                                                       int64_t row0, int64_t Tn, uint32_t mask,
                                                       const TensorScales& ts, const EncTable& tab,
                                                       uint64_t seed, double& g2, double& e2,
                                                       Emit emit) {
-    static_assert(!kFold || (!kSR && !kNoise), "the folded 1/4 is exact for round to nearest only");
+    static_assert(!kFold || (!kNoise && (!kSR || sizeof(T) == 2)),
+                  "the folded 1/4 gives the same codes for bf16 input or round to nearest only");
     uint64_t idx = (uint64_t)f0 * (uint64_t)Tn + (uint64_t)row0;    // SR element index
     Tile16x8<T> sgn = tile;
     sgn.apply_signs(__builtin_amdgcn_readfirstlane(mask));     // the same in every lane
@@ -585,7 +592,7 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
         };
         const uint32_t mask = rht_sign_mask(sign_seed);
         // the fold for bf16 input (the fp32 tile leaves no registers for a second code path)
-        constexpr bool kFoldable = !kSR && sizeof(T) == 2;
+        constexpr bool kFoldable = sizeof(T) == 2;
         if (kFoldable && At <= 0x1p120f)       // the same branch in every lane
             quant_tile_transposed<T, kSR, false, decltype(to_stage), kFoldable>(
                 tile, f0, row0, Tn, mask, tst, tab_t, seed_t, g2, e2, to_stage);
