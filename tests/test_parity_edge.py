@@ -3,8 +3,8 @@ inputs from workloads.edge_fp32: fp32 subnormals with the tensor amax below the 
 threshold, an amax just above it, an amax near the top of the fp32 range, blocks whose E4M3 scale
 is subnormal or zero next to large blocks, signed zeros, subnormal values beside normal ones, and
 Hadamard-transformed amaxes just below and above 2^120; the same tensors in bf16 through the
-Hadamard, dual and MXFP4 dual quantizers (whose bf16 round-to-nearest path folds the transform's
-1/4 into the encode factor while the amax is at most 2^120).  Every quantizer's codes, scale
+Hadamard, dual and MXFP4 dual quantizers (whose bf16 path folds the transform's 1/4 into the
+encode factor while the amax is at most 2^120, for both roundings).  Every quantizer's codes, scale
 bytes, amax and s_dec must equal the oracle's bit for bit; dequantized values exactly; a GEMM of
 each tensor with a normal weight within relative L2 1e-5."""
 import numpy as np
