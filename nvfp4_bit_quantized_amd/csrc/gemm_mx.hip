@@ -299,7 +299,8 @@ struct MxDma2 {
 // one word (one v_perm), so that sub-step s finds its block in byte s for both halves and the
 // MFMA selects it with op_sel = s (no per-sub-step scale read or byte extract).  At s = 1 the
 // words are copied from the other fragment set `prev`, which holds sub-step 0 of the same step;
-// at s = 2 and 3 the set still holds this step's words from s = 0 or 1.
+// at s = 2 and 3 the set still holds this step's words from s = 0 or 1.  The main loop takes
+// s = 0 in two parts instead (d2_read_frags0, d2_gather_scales, below).
 template <int TM, int TN>
 __device__ __forceinline__ void d2_read_frags(const MxStage2& st, MxFrags<TM, TN>& f,
                                               const MxFrags<TM, TN>& prev, int wm, int wn,
@@ -320,6 +321,46 @@ __device__ __forceinline__ void d2_read_frags(const MxStage2& st, MxFrags<TM, TN
         if (s == 0) f.eb[j] = __builtin_amdgcn_perm(st.sb[1][r], st.sb[0][r], sel);
         if (s == 1) f.eb[j] = prev.eb[j];
     }
+}
+
+// Sub-step 0 of a step, split in two so that no wave waits on LDS at the top of a step: the
+// fragment codes and the rows' raw scale words are read right after the barrier, and the
+// gather of a lane's four scale bytes into one word (d2_gather_scales) runs after the previous
+// step's deferred MFMAs have been issued, by when the words have arrived.  Same results as
+// d2_read_frags at s = 0.
+template <int TM, int TN>
+struct MxRawScales {
+    uint32_t a[TM][2], b[TN][2];
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void d2_read_frags0(const MxStage2& st, MxFrags<TM, TN>& f,
+                                               MxRawScales<TM, TN>& raw, int wm, int wn, int lane) {
+    const int lrow = lane & 31, q = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * TM * 32 + i * 32 + lrow;
+        f.a[i] = st.a[r * 8 + d2_swz(r, q)];
+        raw.a[i][0] = st.sa[0][r];
+        raw.a[i][1] = st.sa[1][r];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r = wn * TN * 32 + j * 32 + lrow;
+        f.b[j] = st.b[r * 8 + d2_swz(r, q)];
+        raw.b[j][0] = st.sb[0][r];
+        raw.b[j][1] = st.sb[1][r];
+    }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void d2_gather_scales(MxFrags<TM, TN>& f, const MxRawScales<TM, TN>& raw,
+                                                 int lane) {
+    const uint32_t sel = (lane >> 5) ? 0x07050301u : 0x06040200u;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.ea[i] = __builtin_amdgcn_perm(raw.a[i][1], raw.a[i][0], sel);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.eb[j] = __builtin_amdgcn_perm(raw.b[j][1], raw.b[j][0], sel);
 }
 
 // Workgroups [0, full) compute whole tiles; with a split plan, workgroup full + u computes part
@@ -369,10 +410,11 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
     for (int i = 0; i < TM; ++i) { f1.a[i] = make_uint4(0, 0, 0, 0); f1.ea[i] = 0x7F7F7F7Fu; }
 #pragma unroll
     for (int j = 0; j < TN; ++j) { f1.b[j] = make_uint4(0, 0, 0, 0); f1.eb[j] = 0x7F7F7F7Fu; }
+    MxRawScales<TM, TN> raw;
     wait_vmcnt<0>();
     lds_barrier();
     dma.issue(1, lds0 + sizeof(MxStage2), wave);
-    d2_read_frags<TM, TN>(st[0], f0, f1, wm, wn, lane, 0);
+    d2_read_frags0<TM, TN>(st[0], f0, raw, wm, wn, lane);
     // Step kt multiplies stage kt % 2 while step kt + 1 lands in the other; after the barrier
     // that ends step kt (all reads of its stage done) step kt + 2 is fetched into it.
     int cs = 0;
@@ -380,6 +422,7 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
         const MxStage2& cur = st[cs];
         mx_mfma<TM, TN, kT, 3>(f1, acc);                // previous step, sub-step 3
         __builtin_amdgcn_sched_barrier(0);
+        d2_gather_scales<TM, TN>(f0, raw, lane);
         d2_read_frags<TM, TN>(cur, f1, f0, wm, wn, lane, 1);
         mx_mfma<TM, TN, kT, 0>(f0, acc);                // sub-step 0
         __builtin_amdgcn_sched_barrier(0);
@@ -393,7 +436,8 @@ k_gemm_mxfp4_d2(MxOperand A, MxOperand B, int M, int N, int K, void* __restrict_
         lds_barrier();
         dma.issue(kt + 2, lds0 + cs * (uint32_t)sizeof(MxStage2), wave);
         cs ^= 1;
-        d2_read_frags<TM, TN>(st[cs], f0, f1, wm, wn, lane, 0);
+        d2_read_frags0<TM, TN>(st[cs], f0, raw, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);              // issue the reads before the MFMAs
     }
     mx_mfma<TM, TN, kT, 3>(f1, acc);                    // sub-step 3 of the last step
     wait_vmcnt<0>();                                    // the clamped re-fetches past the end
