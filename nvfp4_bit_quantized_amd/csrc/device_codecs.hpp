@@ -104,9 +104,9 @@ __device__ __forceinline__ void block_scale_tab(float amax_b, const TensorScales
 // with a unit scale performs exactly this rounding for every finite fp32 input.
 __device__ __forceinline__ uint32_t e2m1_rne_pack8(const float* z) {
     // each conversion writes one byte of w and keeps the other three, so the four together
-    // overwrite all of it: w's starting value is never seen (no instruction to set it)
-    uint32_t w = 0;
-    w = __builtin_nondeterministic_value(w);
+    // overwrite all of it: w's starting value is never seen.  Starting from z[0]'s bits lets the
+    // first conversion write over z[0]'s register, where an unset start would cost a move.
+    uint32_t w = __float_as_uint(z[0]);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[0], z[1], 1.0f, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[2], z[3], 1.0f, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, z[4], z[5], 1.0f, 2);
@@ -200,9 +200,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// DPP swap of adjacent lanes (quad_perm [1,0,3,2]).
+// DPP swap of adjacent lanes (quad_perm [1,0,3,2]).  Every caller has both lanes of a pair
+// active, so no lane reads a disabled one; bound_ctrl lets the compiler fold the move into the
+// instruction that consumes it (v_max_f32 with a DPP source).
 __device__ __forceinline__ float swap_adjacent(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
+// DPP swap of lane pairs within a quad (quad_perm [2,3,0,1]); the same conditions, for all four
+// lanes of a quad.
+__device__ __forceinline__ float swap_pairs(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
 
 }  // namespace nvfp4

@@ -501,17 +501,43 @@ template <bool kSR> constexpr int dual_tile_tokens() { return kSR ? 128 : 256; }
 
 // Write-out of a staged tile (every thread of the workgroup calls these after the barrier).
 // Transposed codes: 256 feature rows x kTok / 2 bytes, 8 bytes (16 tokens) per lane, whole rows
-// of the tile per wave instruction; T % 16 == 0 keeps every piece whole and 8-byte aligned.
+// of the tile per wave instruction; T % 16 == 0 keeps every piece whole and 8-byte aligned.  A
+// thread keeps one piece position q and walks down the feature rows, kThreads / kPieces rows a
+// pass, with its destination advanced by a constant instead of recomputed.
 template <int kTok>
 __device__ __forceinline__ void write_staged_cols(const uint32_t* cols, uint8_t* __restrict__ codes_t,
                                                   int64_t tf, int64_t tt, int64_t F, int64_t Tn) {
-    constexpr uint32_t kThreads = 2 * kTok, kPieces = kTok / 16;
-#pragma unroll 2
-    for (uint32_t j = threadIdx.x; j < kDualFeat * kPieces; j += kThreads) {
-        const uint32_t p = j / kPieces, q = j % kPieces;
-        if (tf + p < F && tt + q * 16 < Tn)
-            *reinterpret_cast<uint2*>(codes_t + (tf + p) * (Tn / 2) + tt / 2 + q * 8) =
-                *reinterpret_cast<const uint2*>(&cols[col_slot<kTok>(p, q)]);
+    constexpr uint32_t kThreads = 2 * kTok, kPieces = kTok / 16, kStride = kThreads / kPieces;
+    static_assert(kThreads % kPieces == 0 && kDualFeat % kStride == 0, "passes");
+    const uint32_t q = threadIdx.x % kPieces, p0 = threadIdx.x / kPieces;
+    if (tt + q * 16 >= Tn) return;
+    uint8_t* dst = codes_t + (tf + p0) * (Tn / 2) + tt / 2 + q * 8;
+    const int64_t step = (int64_t)kStride * (Tn / 2);
+#pragma unroll
+    for (uint32_t i = 0; i < kDualFeat / kStride; ++i) {
+        const uint32_t p = p0 + i * kStride;
+        if (tf + p < F)
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&cols[col_slot<kTok>(p, q)]);
+        dst += step;
+    }
+}
+
+// Row-wise codes: kTok token rows x 128 bytes (256 features), 16 lanes per token row, 8 bytes
+// (16 features) each; F % 16 == 0 keeps every piece whole.  Same walk as write_staged_cols.
+template <int kTok>
+__device__ __forceinline__ void write_staged_rows(const uint32_t* rows, uint8_t* __restrict__ codes,
+                                                  int64_t tf, int64_t tt, int64_t F, int64_t Tn) {
+    constexpr uint32_t kThreads = 2 * kTok, kStride = kThreads / 16;
+    const uint32_t q = threadIdx.x & 15u, r0 = threadIdx.x >> 4;
+    if (tf + q * 16 >= F) return;
+    uint8_t* dst = codes + (tt + r0) * (F / 2) + tf / 2 + q * 8;
+    const int64_t step = (int64_t)kStride * (F / 2);
+#pragma unroll
+    for (uint32_t i = 0; i < kTok / kStride; ++i) {
+        const uint32_t r = r0 + i * kStride;
+        if (tt + r < Tn)
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(&rows[row_slot(r) + 2 * q]);
+        dst += step;
     }
 }
 
@@ -604,14 +630,7 @@ k_dual_quant(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint64_
     write_staged_cols<kTok>(stg.cols, codes_t, tf, tt, F, Tn);
     write_staged_scales<kThreads>(stg.csc, kDualFeat, kPieces, scales_t, Tn / 16, tf, F, tt / 16);
     if constexpr (kRows) {
-        // row-wise codes: 16 lanes per token row, 8 bytes (16 features) each; F % 16 == 0
-#pragma unroll 2
-        for (uint32_t j = threadIdx.x; j < kTok * 16; j += kThreads) {
-            const uint32_t r = j >> 4, q = j & 15u;
-            if (tt + r < Tn && tf + q * 16 < F)
-                *reinterpret_cast<uint2*>(codes + (tt + r) * (F / 2) + tf / 2 + q * 8) =
-                    *reinterpret_cast<const uint2*>(&stg.rows[row_slot(r) + 2 * q]);
-        }
+        write_staged_rows<kTok>(stg.rows, codes, tf, tt, F, Tn);
         write_staged_scales<kThreads>(stg.rsc, kTok, 16, scales, F / 16, tt, Tn, tf / 16);
     }
 }
@@ -742,7 +761,7 @@ k_mx_quant_dual(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint
 #pragma unroll
             for (int f = 0; f < 8; ++f) m = fmaxf(m, fabsf(y[f]));
             m = fmaxf(m, swap_adjacent(m));
-            m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));
+            m = fmaxf(m, swap_pairs(m));
             const int e8 = mx_exponent(m);
             float z[8];
 #pragma unroll
@@ -765,13 +784,7 @@ k_mx_quant_dual(const T* __restrict__ x, int64_t Tn, int64_t F, int64_t ld, uint
     __syncthreads();
     write_staged_cols<kTok>(cols, codes_t, tf, tt, F, Tn);
     write_staged_scales<kThreads>(csc, kDualFeat, kBlocks, scales_t, Tn / 32, tf, F, tt / 32);
-#pragma unroll 2
-    for (uint32_t j = threadIdx.x; j < kTok * 16; j += kThreads) {
-        const uint32_t r = j >> 4, q = j & 15u;
-        if (tt + r < Tn && tf + q * 16 < F)
-            *reinterpret_cast<uint2*>(codes + (tt + r) * (F / 2) + tf / 2 + q * 8) =
-                *reinterpret_cast<const uint2*>(&rows[row_slot(r) + 2 * q]);
-    }
+    write_staged_rows<kTok>(rows, codes, tf, tt, F, Tn);
     write_staged_scales<kThreads>(rsc, kTok, kDualFeat / 32, scales, F / 32, tt, Tn, tf / 32);
 }
 

@@ -399,7 +399,7 @@ k_mx_quant(const T* __restrict__ x, int64_t ld, uint32_t groups, FastDiv gpr, ui
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(y[u][e]));
         m = fmaxf(m, swap_adjacent(m));
-        m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));
+        m = fmaxf(m, swap_pairs(m));
         int e8 = 0;
         if (m > 0.0f) {
             e8 = __builtin_amdgcn_frexp_expf(m) - 1 - 2;   // m = f 2^E, f in [0.5, 1)
