@@ -93,6 +93,18 @@ def student_t(shape, nu: float, seed: int, dtype: torch.dtype = torch.bfloat16) 
     return _finish(v, shape, dtype)
 
 
+def device_normal_rows(shape, seed: int, device: str = "cuda") -> torch.Tensor:
+    """A bf16 tensor too large to draw on the host in reasonable time (billions of elements):
+    N(0, 1) drawn by torch's generator on the device, each row times 2^k with k uniform in
+    [-12, 12] (exact in bf16), so that block scales span a wide range.  Seeded and deterministic;
+    the oracle takes a host copy of the same tensor."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.bfloat16)
+    k = torch.randint(-12, 13, (shape[0], 1), generator=g, device=device)
+    x.mul_(torch.exp2(k.to(torch.float32)).to(torch.bfloat16))
+    return x
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """numpy view for the oracle: float32 as is, bf16 as its raw uint16 bit patterns."""
     t = t.detach().contiguous().cpu()
