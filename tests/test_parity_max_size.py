@@ -113,3 +113,23 @@ def test_mx_quantizer(nv, orc, big):
     np.testing.assert_array_equal(_rows(q.scales, ROWS), o["scales"])
     log("mx ok")
     del q
+
+
+def test_gemm_with_operand_past_2gib(nv, orc, big):
+    """The same tensor as the A operand of a GEMM (K = 8192: 2.1 GB of codes, rows past the
+    2 GiB byte offset) against a 256-row weight: sampled output rows within the GEMM bar of the
+    float64 oracle on the oracle's quantization of those rows and of the weight."""
+    from gemm_check import assert_gemm_close
+    x, xh, A = big
+    N = 256
+    w = W.weight((N, F), 20261204)
+    qa = nv.quantize_1d(x, nv.RNE)
+    qb = nv.quantize_1d(w.to(x.device), nv.RNE)
+    c = nv.gemm(qa, qb)                                  # fp32 [T x 256]
+    torch.cuda.synchronize()
+    oa = orc.quantize_1d(np.ascontiguousarray(xh[ROWS]), 0, amax_in=A)
+    ob = orc.quantize_1d(W.bits(w), 0)
+    ref = orc.gemm_f64(oa, ob, len(ROWS), N, F)
+    assert_gemm_close(_rows(c, ROWS), ref, "gemm rows past 2 GiB")
+    log("gemm ok")
+    del qa, qb, c
