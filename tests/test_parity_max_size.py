@@ -133,3 +133,37 @@ def test_gemm_with_operand_past_2gib(nv, orc, big):
     assert_gemm_close(_rows(c, ROWS), ref, "gemm rows past 2 GiB")
     log("gemm ok")
     del qa, qb, c
+
+
+def test_gemm_with_output_past_2_31_elements(nv, orc, big):
+    """C = x W^T with W 8192 x 8192: 4.3e9 outputs (17 GB in fp32, 8.6 GB in bf16).  Sampled
+    output rows (those around output element 2^31 and 2^32 included) meet the GEMM bar in fp32;
+    the bf16 output equals the fp32 one rounded to nearest even, and is within one bf16 ulp of
+    the oracle's float64 result rounded to bf16 (equal for at least 99.9%)."""
+    from gemm_check import assert_gemm_close
+    x, xh, A = big
+    N = F
+    w = W.weight((N, F), 20261205)
+    qa = nv.quantize_1d(x, nv.RNE)
+    qb = nv.quantize_1d(w.to(x.device), nv.RNE)
+    oa = orc.quantize_1d(np.ascontiguousarray(xh[ROWS]), 0, amax_in=A)
+    ob = orc.quantize_1d(W.bits(w), 0)
+    ref = orc.gemm_f64(oa, ob, len(ROWS), N, F)
+    c = nv.gemm(qa, qb)
+    torch.cuda.synchronize()
+    got = _rows(c, ROWS)
+    del c
+    assert_gemm_close(got, ref, "fp32 output rows past 2^31 elements")
+    cb = nv.gemm(qa, qb, torch.bfloat16)
+    torch.cuda.synchronize()
+    gb = torch.from_numpy(_rows(cb.view(torch.int16), ROWS)).view(torch.bfloat16)
+    del cb
+    assert torch.equal(gb.view(torch.int16), torch.from_numpy(got).to(torch.float32)
+                       .to(torch.bfloat16).view(torch.int16))
+    rb = torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16)
+    equal = gb.float() == rb.float()
+    ulps = torch.where(equal, torch.zeros(equal.shape, dtype=torch.int32),
+                       (gb.view(torch.int16).to(torch.int32) - rb.view(torch.int16).to(torch.int32)).abs())
+    assert int(ulps.max()) <= 1 and float((ulps == 0).float().mean()) >= 0.999
+    log("gemm output ok")
+    del qa, qb
