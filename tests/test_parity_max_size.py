@@ -167,3 +167,22 @@ def test_gemm_with_output_past_2_31_elements(nv, orc, big):
     assert int(ulps.max()) <= 1 and float((ulps == 0).float().mean()) >= 0.999
     log("gemm output ok")
     del qa, qb
+
+
+def test_mx_gemm_with_operand_past_2gib(nv, orc, big):
+    """The MXFP4 comparison GEMM on the same tensor (2.1 GB of codes fetched straight into LDS)
+    against a 256-row weight: sampled output rows within the GEMM bar of the oracle."""
+    from gemm_check import assert_gemm_close
+    x, xh, A = big
+    N = 256
+    w = W.weight((N, F), 20261206)
+    qa = nv.mx_quantize_1d(x, nv.RNE)
+    qb = nv.mx_quantize_1d(w.to(x.device), nv.RNE)
+    c = nv.mx_gemm(qa, qb)
+    torch.cuda.synchronize()
+    oa = orc.mx_quantize_1d(np.ascontiguousarray(xh[ROWS]), 0)
+    ob = orc.mx_quantize_1d(W.bits(w), 0)
+    ref = orc.mx_gemm_f64(oa, ob, len(ROWS), N, F)
+    assert_gemm_close(_rows(c, ROWS), ref, "mx gemm rows past 2 GiB")
+    log("mx gemm ok")
+    del qa, qb, c
